@@ -1,0 +1,164 @@
+"""Exact-attention oracle: plain fp64 CPU reference (ctypes over ``oracle.c``).
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of ``bench.py`` may import this package. The product path
+(``exact_attention_106_amd``) never imports it, and this package imports
+nothing from the product: the two share no code.
+
+Every function here computes the plain definition of attention in fp64
+(scores, 3-pass safe softmax, weighted sum, logsumexp); see ``oracle.c`` for
+the passages each step follows. ``online.py`` holds the pages' tiled
+online-softmax algorithm, used only to pin this oracle against the pages.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile ``oracle.c`` with gcc (fp64, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH) or (
+        os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)
+    ):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+               "-fno-fast-math", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            lib = ctypes.CDLL(_LIB_PATH)
+            dp = ctypes.POINTER(ctypes.c_double)
+            lp = ctypes.POINTER(ctypes.c_long)
+            L, I, D = ctypes.c_long, ctypes.c_int, ctypes.c_double
+            vp = ctypes.c_void_p
+            lib.oracle_attention.argtypes = [dp, dp, dp, dp, dp, L, L, L, I, D, I]
+            lib.oracle_attention.restype = I
+            lib.oracle_attention_rows.argtypes = [dp, lp, L, dp, dp, L, I, D, I, dp, dp]
+            lib.oracle_attention_rows.restype = I
+            lib.oracle_bf16_to_f64.argtypes = [vp, dp, L]
+            lib.oracle_bf16_to_f64.restype = None
+            lib.oracle_e4m3_to_f64.argtypes = [vp, dp, L]
+            lib.oracle_e4m3_to_f64.restype = None
+            lib.oracle_dequant_e4m3.argtypes = [vp, vp, dp, L, L, I, I]
+            lib.oracle_dequant_e4m3.restype = None
+            lib.oracle_paged_decode.argtypes = [dp, vp, vp, vp, vp, L, I, I, I, L, L, D, dp, dp]
+            lib.oracle_paged_decode.restype = I
+            _lib = lib
+    return _lib
+
+
+def _f64(x) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _dptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def attention(q, k, v, scale: float, causal: bool):
+    """O, L for q/k/v of shape [..., N, d] (leading dims are independent heads).
+
+    Returns (o [..., N, d], lse [..., N]) in fp64.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    if q.ndim < 2 or k.shape != v.shape or q.shape[:-2] != k.shape[:-2] or q.shape[-1] != k.shape[-1]:
+        raise ValueError("shape mismatch")
+    lead = q.shape[:-2]
+    n_q, d = q.shape[-2], q.shape[-1]
+    n_k = k.shape[-2]
+    bh = int(np.prod(lead)) if lead else 1
+    o = np.empty(lead + (n_q, d), dtype=np.float64)
+    lse = np.empty(lead + (n_q,), dtype=np.float64)
+    rc = _load().oracle_attention(_dptr(q), _dptr(k), _dptr(v), _dptr(o), _dptr(lse),
+                                  bh, n_q, n_k, d, float(scale), int(bool(causal)))
+    if rc != 0:
+        raise RuntimeError("oracle_attention failed (%d)" % rc)
+    return o, lse
+
+
+def attention_rows(q_rows, pos, k, v, scale: float, causal: bool):
+    """Selected query rows of one head: q_rows [R, d] at positions pos [R]; k/v [N, d]."""
+    q_rows, k, v = _f64(q_rows), _f64(k), _f64(v)
+    pos = np.ascontiguousarray(np.asarray(pos, dtype=np.int64))
+    r, d = q_rows.shape
+    o = np.empty((r, d), dtype=np.float64)
+    lse = np.empty((r,), dtype=np.float64)
+    rc = _load().oracle_attention_rows(
+        _dptr(q_rows), pos.ctypes.data_as(ctypes.POINTER(ctypes.c_long)), r,
+        _dptr(k), _dptr(v), k.shape[0], d, float(scale), int(bool(causal)), _dptr(o), _dptr(lse))
+    if rc != 0:
+        raise RuntimeError("oracle_attention_rows failed (%d)" % rc)
+    return o, lse
+
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """bf16 bit patterns (uint16 array) -> exact fp64 values."""
+    b = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16))
+    out = np.empty(b.shape, dtype=np.float64)
+    _load().oracle_bf16_to_f64(b.ctypes.data, _dptr(out), b.size)
+    return out
+
+
+def e4m3_to_f64(codes) -> np.ndarray:
+    """OCP E4M3FN bytes (uint8 array) -> exact fp64 values (NaN for S.1111.111)."""
+    c = np.ascontiguousarray(np.asarray(codes, dtype=np.uint8))
+    out = np.empty(c.shape, dtype=np.float64)
+    _load().oracle_e4m3_to_f64(c.ctypes.data, _dptr(out), c.size)
+    return out
+
+
+def dequant_e4m3(x8, scales, block: int = 128) -> np.ndarray:
+    """x8 [..., N, d] e4m3 bytes with scales [..., ceil(N/block)] fp32 -> fp64 values."""
+    x = np.ascontiguousarray(np.asarray(x8, dtype=np.uint8))
+    s = np.ascontiguousarray(np.asarray(scales, dtype=np.float32))
+    n, d = x.shape[-2], x.shape[-1]
+    bh = int(np.prod(x.shape[:-2])) if x.ndim > 2 else 1
+    if s.shape[-1] != (n + block - 1) // block or s.size != bh * s.shape[-1]:
+        raise ValueError("scale shape mismatch")
+    out = np.empty(x.shape, dtype=np.float64)
+    _load().oracle_dequant_e4m3(x.ctypes.data, s.ctypes.data, _dptr(out), bh, n, d, block)
+    return out
+
+
+def paged_decode(q, kcache_bits, vcache_bits, block_table, ctx_lens, scale: float):
+    """Decode attention through a block table.
+
+    q [S, H, d] (any float, converted exactly to fp64); kcache/vcache bf16 bit
+    patterns (uint16) [P, H, page_size, d]; block_table int32 [S, max_blocks];
+    ctx_lens int32 [S]. Returns (o [S, H, d], lse [S, H]) in fp64.
+    """
+    q = _f64(q)
+    kc = np.ascontiguousarray(np.asarray(kcache_bits, dtype=np.uint16))
+    vc = np.ascontiguousarray(np.asarray(vcache_bits, dtype=np.uint16))
+    bt = np.ascontiguousarray(np.asarray(block_table, dtype=np.int32))
+    cl = np.ascontiguousarray(np.asarray(ctx_lens, dtype=np.int32))
+    s_, h, d = q.shape
+    p, h2, ps, d2 = kc.shape
+    if (h2, d2) != (h, d) or vc.shape != kc.shape or bt.shape[0] != s_ or cl.shape != (s_,):
+        raise ValueError("shape mismatch")
+    o = np.empty((s_, h, d), dtype=np.float64)
+    lse = np.empty((s_, h), dtype=np.float64)
+    rc = _load().oracle_paged_decode(_dptr(q), kc.ctypes.data, vc.ctypes.data, bt.ctypes.data,
+                                     cl.ctypes.data, s_, h, d, ps, bt.shape[1], p, float(scale),
+                                     _dptr(o), _dptr(lse))
+    if rc != 0:
+        raise RuntimeError("oracle_paged_decode failed (%d)" % rc)
+    return o, lse
