@@ -1,0 +1,213 @@
+"""Benchmark of the fused attention hot path on one MI355X.
+
+One step = one pass of the whole path over resident synthetic inputs:
+  1. fa_fwd      bf16 causal prefill, B=1 H=32 N=16384 d=128   (headline)
+  2. fa_fwd_fp8  E4M3 causal prefill, B=2 H=16 N=8192 d=128
+  3. fa_paged_decode  64 sequences, H=32, d=128, contexts 512..32768
+Each launch is bracketed by HIP events on the stream it runs on. `value` is
+the prefill's TFLOP/s (4*B*H*N^2*d, halved for causal, per the kernel's mean
+event time); decode GB/s and fp8 TFLOP/s are reported beside it. The CPU
+baseline is the fp64 oracle, timed on a bounded sample of the prefill
+workload on this host's cores.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP8_TFLOPS = 5000.0
+PEAK_HBM_GBS = 8000.0
+METRIC = "attention fwd TFLOP/s & % MFMA peak (N=16k,d=128 causal); decode HBM GB/s"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def prefill_flops(B, H, N, d, causal):
+    f = 4.0 * B * H * N * N * d
+    return f / 2 if causal else f
+
+
+def decode_bytes(p):
+    """Algorithmic HBM bytes of one decode: every unique (page, head) slot of a
+    valid token read once for K and once for V, plus q, O, L and the table
+    entries read. Also returns the logical (per-sequence) count."""
+    import numpy as np
+    ctx = p.ctx_lens.cpu().numpy().astype(np.int64)
+    bt = p.block_table.cpu().numpy()
+    S, H, d = p.q.shape
+    per_tok = 2 * H * d * 2                      # K and V, all heads, bf16
+    logical_tok = int(ctx.sum())
+    seen = {}
+    for s in range(S):
+        nb = (int(ctx[s]) + 15) // 16
+        for b in range(nb):
+            valid = min(16, int(ctx[s]) - 16 * b)
+            pg = int(bt[s, b])
+            seen[pg] = max(seen.get(pg, 0), valid)
+    unique_tok = sum(seen.values())
+    fixed = S * H * d * 2 * 2 + S * H * 4 + int(((ctx + 15) // 16).sum()) * 4 + S * 4
+    return unique_tok * per_tok + fixed, logical_tok * per_tok + fixed
+
+
+def cpu_baseline(x, budget_s=15.0):
+    """Time the fp64 oracle on a bounded sample of the causal prefill: query rows
+    i = 7 mod 8 of the first h heads, h chosen so the run takes about budget_s."""
+    import numpy as np
+    import oracle
+    B, H, N, d = x.q.shape
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    stride = 8
+    rows = np.arange(stride - 1, N, stride)
+
+    def head_f64(t, h):
+        return oracle.bf16_bits_to_f64(t[0, h].contiguous().view(__import__("torch").int16).numpy().view(np.uint16))
+
+    def run(heads):
+        flops = 0.0
+        t = 0.0
+        for h in heads:
+            q, k, v = head_f64(x.q, h), head_f64(x.k, h), head_f64(x.v, h)
+            t0 = time.perf_counter()
+            oracle.attention_rows(q[rows], rows, k, v, x.scale, True)
+            t += time.perf_counter() - t0
+            flops += float(np.sum(4.0 * d * (rows + 1)))
+        return flops, t
+
+    f1, t1 = run([0])
+    n_heads = max(1, min(H, int(budget_s / max(t1, 1e-3))))
+    f, t = run(list(range(1, n_heads + 1))[: H - 1] or [0])
+    f += f1
+    t += t1
+    n_used = 1 + min(n_heads, H - 1)
+    return {"value": f / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "fp64 oracle, causal B1 H32 N16384 d128 rows i%%8==7 of %d heads "
+                      "(%d rows, %.3g flop, %.1f s)" % (n_used, n_used * len(rows), f, t)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--only", default="", help="comma list of prefill,fp8,decode (default all)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the path would shard heads / sequences across GPUs with no communication)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import exact_attention_106_amd as fa
+    from exact_attention_106_amd import inputs
+
+    only = set(filter(None, args.only.split(","))) or {"prefill", "fp8", "decode"}
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    fa.fa_version()
+
+    log("generating inputs")
+    parts = []
+    if "prefill" in only:
+        x3 = inputs.config3()
+        q3, k3, v3 = x3.q.to(dev), x3.k.to(dev), x3.v.to(dev)
+        o3 = torch.empty_like(q3)
+        l3 = torch.empty(q3.shape[:3], dtype=torch.float32, device=dev)
+        parts.append(("prefill", lambda: fa.fa_fwd(q3, k3, v3, scale=x3.scale, causal=True, out=o3, lse=l3)))
+    if "fp8" in only:
+        x4 = inputs.config4()
+        t4 = [t.to(dev) for t in (x4.q8, x4.k8, x4.v8, x4.q_scale, x4.k_scale, x4.v_scale)]
+        o4 = torch.empty(x4.q8.shape, dtype=torch.bfloat16, device=dev)
+        l4 = torch.empty(x4.q8.shape[:3], dtype=torch.float32, device=dev)
+        parts.append(("fp8", lambda: fa.fa_fwd_fp8(*t4, scale=x4.scale, causal=True, out=o4, lse=l4)))
+    if "decode" in only:
+        p5 = inputs.config5(device=dev)
+        ws = torch.empty(fa.fa_paged_decode_workspace_bytes(64, 32, 128, 16, p5.block_table.shape[1]),
+                         dtype=torch.uint8, device=dev)
+        o5 = torch.empty(p5.q.shape, dtype=torch.bfloat16, device=dev)
+        l5 = torch.empty(p5.q.shape[:2], dtype=torch.float32, device=dev)
+        parts.append(("decode", lambda: fa.fa_paged_decode(p5.q, p5.kcache, p5.vcache, p5.block_table,
+                                                           p5.ctx_lens, scale=p5.scale, workspace=ws,
+                                                           out=o5, lse=l5)))
+    torch.cuda.synchronize()
+
+    log("warmup %d" % args.warmup)
+    for _ in range(args.warmup):
+        for _, fn in parts:
+            fn()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev = {name: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(args.steps)] for name, _ in parts}
+    log("timing %d steps" % args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        for name, fn in parts:
+            a, b = ev[name][i]
+            a.record(stream)
+            fn()
+            b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = {name: sum(a.elapsed_time(b) for a, b in ev[name]) / args.steps for name, _ in parts}
+    log("mean ms per launch: %s" % ms)
+
+    result = {"metric": METRIC, "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+              "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True,
+              "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+              "data": "synthetic (seeded N(0,1); fp8 with outliers, Haar rotation, block E4M3; "
+                      "paged pool with shared prefixes)",
+              "config": {"workload": "causal bf16 prefill B1 H32 N16384 d128 + fp8 causal prefill "
+                                     "B2 H16 N8192 d128 + paged decode S64 H32 d128 ctx 512..32768",
+                         "global_batch": 1, "seq_len": 16384, "parallelism": "single GPU"}}
+    if "prefill" in ms:
+        f = prefill_flops(1, 32, 16384, 128, True)
+        tf = f / (ms["prefill"] * 1e-3) / 1e12
+        result["value"] = tf
+        result["roofline"] = {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS,
+                              "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS, "traffic": None,
+                              "kernel": "fwd_bf16_kernel<128,true>", "launch_ms": ms["prefill"],
+                              "flop_per_launch": f}
+    if "fp8" in ms:
+        f = prefill_flops(2, 16, 8192, 128, True)
+        tf = f / (ms["fp8"] * 1e-3) / 1e12
+        result["fp8"] = {"value": tf, "unit": "TFLOP/s", "launch_ms": ms["fp8"],
+                         "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP8_TFLOPS,
+                                      "unit": "TFLOP/s", "frac": tf / PEAK_FP8_TFLOPS, "traffic": None,
+                                      "kernel": "fwd_fp8_kernel<true>"}}
+    if "decode" in ms:
+        ub, lb = decode_bytes(p5)
+        gbs = ub / (ms["decode"] * 1e-3) / 1e9
+        result["decode"] = {"value": gbs, "unit": "GB/s", "launch_ms": ms["decode"],
+                            "bytes_unique": ub, "bytes_logical": lb,
+                            "logical_GBps": lb / (ms["decode"] * 1e-3) / 1e9,
+                            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
+                                         "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "traffic": None,
+                                         "kernel": "decode_split_kernel + decode_merge_kernel"}}
+    if result["value"] is None and "decode" in result:
+        result["value"], result["unit"] = result["decode"]["value"], "GB/s"
+    if not args.no_cpu_baseline and "prefill" in only:
+        log("cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(x3, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,1 +1,183 @@
-"""MI355X-native fused exact attention (placeholder; binding added with the library)."""
+"""MI355X (gfx950) fused exact attention: Python binding of libfa.so.
+
+The functions carry the names of the C ABI in ``include/fa.h`` and only
+marshal arguments: they check devices, dtypes and shapes, allocate outputs
+with torch when the caller passes none, and call the library on the current
+HIP stream. Every step of the computation runs in the library's HIP kernels;
+there is no fallback. Importing this package does not load the library; the
+first call does, and raises if it has not been built.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import FaError
+
+__all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_paged_decode",
+           "fa_paged_decode_workspace_bytes", "fa_status_str", "fa_version", "FaError"]
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t: torch.Tensor):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _check_dev(name, t, dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a device (cuda/HIP) tensor" % name)
+    if t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError("%s must have dtype %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+def _dense_common(q, k, v, dtype, out, lse, out_dtype):
+    _check_dev("q", q, dtype)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    _check_dev("k", k, dtype, q.shape)
+    _check_dev("v", v, dtype, q.shape)
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k, v must be on one device")
+    B, H, N, d = q.shape
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=out_dtype, device=q.device)
+    _check_dev("out", out, out_dtype, (B, H, N, d))
+    if lse is not None:
+        _check_dev("lse", lse, torch.float32, (B, H, N))
+    return B, H, N, d, out
+
+
+def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float] = None,
+           causal: bool = False, out: Optional[torch.Tensor] = None,
+           lse: Optional[torch.Tensor] = None, return_lse: bool = True
+           ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """bf16 fused attention forward. q/k/v bf16 [B, H, N, d], d in {64, 128}.
+    Returns (O bf16 [B, H, N, d], L fp32 [B, H, N] or None)."""
+    B, H, N, d, out = _dense_common(q, k, v, torch.bfloat16, out, lse, torch.bfloat16)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = _lib.load().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, scale,
+                            int(bool(causal)), _stream(q))
+    _lib.check(st, "fa_fwd")
+    return out, lse
+
+
+def fa_fwd_f32(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float] = None,
+               causal: bool = False, out: Optional[torch.Tensor] = None,
+               lse: Optional[torch.Tensor] = None, return_lse: bool = True
+               ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """fp32 fused attention forward, 1 <= d <= 128."""
+    B, H, N, d, out = _dense_common(q, k, v, torch.float32, out, lse, torch.float32)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = _lib.load().fa_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, scale,
+                                int(bool(causal)), _stream(q))
+    _lib.check(st, "fa_fwd_f32")
+    return out, lse
+
+
+def _as_u8(name, t):
+    if isinstance(t, torch.Tensor) and t.dtype == torch.float8_e4m3fn:
+        t = t.view(torch.uint8)
+    _check_dev(name, t, torch.uint8)
+    return t
+
+
+def fa_fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, q_scale: torch.Tensor,
+               k_scale: torch.Tensor, v_scale: torch.Tensor, scale: Optional[float] = None,
+               causal: bool = False, out: Optional[torch.Tensor] = None,
+               lse: Optional[torch.Tensor] = None, return_lse: bool = True
+               ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """FP8 (E4M3FN) fused attention forward with fp32 scales per (b, h, 128-token block).
+    q8/k8/v8 uint8 or float8_e4m3fn [B, H, N, 128]; scales fp32 [B, H, ceil(N/128)]."""
+    q8, k8, v8 = _as_u8("q8", q8), _as_u8("k8", k8), _as_u8("v8", v8)
+    if q8.dim() != 4:
+        raise ValueError("q8 must be [B, H, N, d]")
+    B, H, N, d = q8.shape
+    _check_dev("k8", k8, torch.uint8, q8.shape)
+    _check_dev("v8", v8, torch.uint8, q8.shape)
+    nsb = (N + 127) // 128
+    for nm, s in (("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)):
+        _check_dev(nm, s, torch.float32, (B, H, nsb))
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
+    _check_dev("out", out, torch.bfloat16, (B, H, N, d))
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    if lse is not None:
+        _check_dev("lse", lse, torch.float32, (B, H, N))
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = _lib.load().fa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scale), _ptr(k_scale),
+                                _ptr(v_scale), _ptr(out), _ptr(lse), B, H, N, d, scale,
+                                int(bool(causal)), _stream(q8))
+    _lib.check(st, "fa_fwd_fp8")
+    return out, lse
+
+
+def fa_paged_decode_workspace_bytes(num_seqs: int, H: int, d: int, page_size: int,
+                                    max_blocks_per_seq: int) -> int:
+    return int(_lib.load().fa_paged_decode_workspace_bytes(num_seqs, H, d, page_size,
+                                                           max_blocks_per_seq))
+
+
+def fa_paged_decode(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
+                    block_table: torch.Tensor, ctx_lens: torch.Tensor,
+                    scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
+                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                    return_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Paged-KV decode. q bf16 [S, H, d]; caches bf16 [P, H, page_size, d];
+    block_table int32 [S, max_blocks]; ctx_lens int32 [S]."""
+    _check_dev("q", q, torch.bfloat16)
+    if q.dim() != 3:
+        raise ValueError("q must be [S, H, d]")
+    S, H, d = q.shape
+    _check_dev("kcache", kcache, torch.bfloat16)
+    if kcache.dim() != 4 or kcache.shape[1] != H or kcache.shape[3] != d:
+        raise ValueError("kcache must be [P, H, page_size, d]")
+    _check_dev("vcache", vcache, torch.bfloat16, kcache.shape)
+    P, _, page_size, _ = kcache.shape
+    _check_dev("block_table", block_table, torch.int32)
+    if block_table.dim() != 2 or block_table.shape[0] != S:
+        raise ValueError("block_table must be [S, max_blocks]")
+    _check_dev("ctx_lens", ctx_lens, torch.int32, (S,))
+    max_blocks = block_table.shape[1]
+    need = fa_paged_decode_workspace_bytes(S, H, d, page_size, max_blocks)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=q.device)
+    _check_dev("workspace", workspace, torch.uint8)
+    if out is None:
+        out = torch.empty((S, H, d), dtype=torch.bfloat16, device=q.device)
+    _check_dev("out", out, torch.bfloat16, (S, H, d))
+    if lse is None and return_lse:
+        lse = torch.empty((S, H), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check_dev("lse", lse, torch.float32, (S, H))
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = _lib.load().fa_paged_decode(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(block_table),
+                                     _ptr(ctx_lens), _ptr(out), _ptr(lse), S, H, d, page_size,
+                                     max_blocks, P, scale, _ptr(workspace),
+                                     workspace.numel(), _stream(q))
+    _lib.check(st, "fa_paged_decode")
+    return out, lse
+
+
+def fa_status_str(status: int) -> str:
+    return _lib.status_str(status)
+
+
+def fa_version() -> int:
+    return int(_lib.load().fa_version())

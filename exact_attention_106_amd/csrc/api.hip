@@ -1,0 +1,111 @@
+// C ABI of libfa.so: argument checks on the host, then one launcher per entry
+// point. Nothing here allocates, synchronises or reads device memory.
+#include <math.h>
+
+#include "../../include/fa.h"
+#include "fa_launch.h"
+
+namespace {
+
+constexpr long long kMaxElems = (1LL << 31) - 1;
+
+fa_status from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+bool bad_scale(float scale) { return !(isfinite(scale) && scale > 0.f); }
+
+fa_status check_dense(const void *q, const void *k, const void *v, const void *o, int B, int H,
+                      int N, int d, float scale, int causal)
+{
+    if (!q || !k || !v || !o) return FA_ERR_NULL_PTR;
+    if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return FA_ERR_BAD_SHAPE;
+    if ((long long)B * H * N * d > kMaxElems) return FA_ERR_BAD_SHAPE;
+    if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
+    if (bad_scale(scale)) return FA_ERR_UNSUPPORTED;
+    return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+                 int N, int d, float scale, int causal, void *stream)
+{
+    fa_status st = check_dense(q, k, v, o, B, H, N, d, scale, causal);
+    if (st != FA_OK) return st;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    return from_hip(fa::launch_fwd_bf16(q, k, v, o, lse, B, H, N, d, scale, causal,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_fwd_f32(const float *q, const float *k, const float *v, float *o, float *lse, int B,
+                     int H, int N, int d, float scale, int causal, void *stream)
+{
+    fa_status st = check_dense(q, k, v, o, B, H, N, d, scale, causal);
+    if (st != FA_OK) return st;
+    if (d > 128) return FA_ERR_UNSUPPORTED;
+    return from_hip(fa::launch_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_fwd_fp8(const uint8_t *q8, const uint8_t *k8, const uint8_t *v8, const float *q_scale,
+                     const float *k_scale, const float *v_scale, void *o, float *lse, int B, int H,
+                     int N, int d, float scale, int causal, void *stream)
+{
+    fa_status st = check_dense(q8, k8, v8, o, B, H, N, d, scale, causal);
+    if (st != FA_OK) return st;
+    if (!q_scale || !k_scale || !v_scale) return FA_ERR_NULL_PTR;
+    if (d != 128) return FA_ERR_UNSUPPORTED;
+    return from_hip(fa::launch_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, H, N, d,
+                                       scale, causal, static_cast<hipStream_t>(stream)));
+}
+
+size_t fa_paged_decode_workspace_bytes(int num_seqs, int H, int d, int page_size,
+                                       int max_blocks_per_seq)
+{
+    if (num_seqs <= 0 || H <= 0 || max_blocks_per_seq <= 0) return 0;
+    if (d != 128 || page_size != 16) return 0;
+    return (size_t)num_seqs * H * fa::decode_max_splits(max_blocks_per_seq) *
+           fa::decode_partial_floats(d) * sizeof(float);
+}
+
+fa_status fa_paged_decode(const void *q, const void *kcache, const void *vcache,
+                          const int32_t *block_table, const int32_t *ctx_lens, void *o, float *lse,
+                          int num_seqs, int H, int d, int page_size, int max_blocks_per_seq,
+                          int num_pages, float scale, void *workspace, size_t workspace_bytes,
+                          void *stream)
+{
+    if (!q || !kcache || !vcache || !block_table || !ctx_lens || !o || !workspace)
+        return FA_ERR_NULL_PTR;
+    if (num_seqs <= 0 || H <= 0 || d <= 0 || page_size <= 0 || max_blocks_per_seq <= 0 ||
+        num_pages <= 0)
+        return FA_ERR_BAD_SHAPE;
+    if (d != 128 || page_size != 16) return FA_ERR_UNSUPPORTED;
+    if (num_seqs > 65535 || H > 65535) return FA_ERR_BAD_SHAPE;
+    if ((long long)max_blocks_per_seq * page_size > kMaxElems) return FA_ERR_BAD_SHAPE;
+    if (bad_scale(scale)) return FA_ERR_UNSUPPORTED;
+    if (workspace_bytes < fa_paged_decode_workspace_bytes(num_seqs, H, d, page_size,
+                                                          max_blocks_per_seq))
+        return FA_ERR_WORKSPACE;
+    return from_hip(fa::launch_paged_decode(q, kcache, vcache, block_table, ctx_lens, o, lse,
+                                            num_seqs, H, d, page_size, max_blocks_per_seq, scale,
+                                            static_cast<float *>(workspace),
+                                            static_cast<hipStream_t>(stream)));
+}
+
+const char *fa_status_str(fa_status s)
+{
+    switch (s) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_NULL_PTR: return "FA_ERR_NULL_PTR: a required pointer is NULL";
+    case FA_ERR_BAD_SHAPE: return "FA_ERR_BAD_SHAPE: a size is non-positive or too large";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head size, page size, flag or scale not supported";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace too small";
+    case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported an error";
+    }
+    return "unknown fa_status";
+}
+
+int fa_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,236 @@
+// Paged-KV decode attention, split over KV chunks, then merged (d = 128,
+// 16-token pages).
+//
+// The cache is addressed through a per-sequence block table of fixed-size
+// pages (PagedAttention section of "FlashAttention系列优化"): token t of
+// sequence s is slot t % 16 of physical page block_table[s][t / 16]; pages
+// may be shared between sequences and are only read here.
+//
+// Kernel 1 (split): one workgroup per (KV chunk of 32 pages, head, sequence).
+// Each of its 4 waves walks every 4th page of the chunk. A (page, head) block
+// of K or V is 16 tokens x 128 channels of bf16 = 4 KiB contiguous; a wave
+// reads it with four fully coalesced 1 KiB loads, so lane l holds tokens
+// 4i + l/16 (i = 0..3) at channels 8 (l % 16) .. +7. Scores are reduced over
+// the 16 lanes of a row group; every lane then runs the online-softmax update
+// (running max, unscaled sum, unscaled 8-channel output) over the tokens it
+// sees. The four token groups of a wave and then the four waves are combined
+// with the rescale identity of the FlashAttention-2 accumulator
+// ("FlashAttention系列优化", FlashAttentionV2 equations), and the chunk's
+// partial (m, l, O~) goes to the workspace. This kernel is HBM-bound: the only
+// traffic that matters is reading each needed page once.
+//
+// Kernel 2 (merge): one workgroup per (head, sequence) combines its chunks'
+// partials the same way and writes O (bf16) and L = (m + log2 l) ln 2.
+// Slots past the context in the last page are neither used nor loaded.
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace fa {
+namespace {
+
+constexpr int kD = 128;
+constexpr int kPS = 16;
+constexpr int kPPS = kDecodePagesPerSplit;
+constexpr int kWaves = 4;
+constexpr int kPF = kD + 2;   // floats per partial
+
+struct State {
+    float m, l, o[8];
+};
+
+__device__ __forceinline__ void merge_into(State &a, float m2, float l2, const float *o2) {
+    const float mm = fmaxf(a.m, m2);
+    const float mu = mm == neg_inf() ? 0.f : mm;
+    const float wa = exp2_hw(a.m - mu);
+    const float wb = exp2_hw(m2 - mu);
+    a.l = a.l * wa + l2 * wb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a.o[e] = a.o[e] * wa + o2[e] * wb;
+    a.m = mm;
+}
+
+__global__ __launch_bounds__(256) void decode_split_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc,
+    const int32_t *__restrict__ block_table, const int32_t *__restrict__ ctx_lens,
+    float *__restrict__ ws, int H, int max_blocks, int max_splits, float c)
+{
+    const int split = blockIdx.x;
+    const int h = blockIdx.y;
+    const int s = blockIdx.z;
+    const int ctx = ctx_lens[s];
+    const int n_pages = (ctx + kPS - 1) / kPS;
+    const int p_begin = split * kPPS;
+    if (p_begin >= n_pages) return;   // whole workgroup: chunk past the context
+    const int p_end = min(n_pages, p_begin + kPPS);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int tg = lane >> 4;        // token group: tokens 4i + tg
+    const int d0 = 8 * (lane & 15);  // channels d0 .. d0+7
+
+    // query slice, pre-multiplied by scale * log2 e
+    float qv[8];
+    {
+        const u32x4 raw = *reinterpret_cast<const u32x4 *>(q + ((size_t)s * H + h) * kD + d0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            qv[2 * e] = bf16_lo(raw[e]) * c;
+            qv[2 * e + 1] = bf16_hi(raw[e]) * c;
+        }
+    }
+
+    State st;
+    st.m = neg_inf();
+    st.l = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st.o[e] = 0.f;
+
+    const int32_t *bt = block_table + (size_t)s * max_blocks;
+    for (int pg = p_begin + w; pg < p_end; pg += kWaves) {
+        const int phys = __builtin_amdgcn_readfirstlane(bt[pg]);
+        const size_t base = ((size_t)phys * H + h) * (kPS * kD);
+        const uint16_t *kp = kc + base;
+        const uint16_t *vp = vc + base;
+        const int tok0 = pg * kPS;
+        u32x4 kx[4], vx[4];
+        bool valid[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int tok = 4 * i + tg;
+            valid[i] = tok0 + tok < ctx;
+            kx[i] = valid[i] ? *reinterpret_cast<const u32x4 *>(kp + tok * kD + d0) : u32x4{};
+            vx[i] = valid[i] ? *reinterpret_cast<const u32x4 *>(vp + tok * kD + d0) : u32x4{};
+        }
+        float sc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float a = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                a = fmaf(qv[2 * e], bf16_lo(kx[i][e]), a);
+                a = fmaf(qv[2 * e + 1], bf16_hi(kx[i][e]), a);
+            }
+            // sum over the 16 lanes that share this token
+            a += __shfl_xor(a, 1);
+            a += __shfl_xor(a, 2);
+            a += __shfl_xor(a, 4);
+            a += __shfl_xor(a, 8);
+            sc[i] = valid[i] ? a : neg_inf();
+        }
+        const float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+        const float m_new = fmaxf(st.m, mx);
+        const float mu = m_new == neg_inf() ? 0.f : m_new;
+        const float alpha = exp2_hw(st.m - mu);
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = exp2_hw(sc[i] - mu);
+        st.l = st.l * alpha + (p[0] + p[1]) + (p[2] + p[3]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float lo = st.o[2 * e] * alpha, hi = st.o[2 * e + 1] * alpha;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                lo = fmaf(p[i], bf16_lo(vx[i][e]), lo);
+                hi = fmaf(p[i], bf16_hi(vx[i][e]), hi);
+            }
+            st.o[2 * e] = lo;
+            st.o[2 * e + 1] = hi;
+        }
+        st.m = m_new;
+    }
+
+    // combine the 4 token groups of the wave (lanes l, l^16, l^32, l^48 share channels)
+#pragma unroll
+    for (int off = 16; off <= 32; off <<= 1) {
+        const float m2 = __shfl_xor(st.m, off);
+        const float l2 = __shfl_xor(st.l, off);
+        float o2[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o2[e] = __shfl_xor(st.o[e], off);
+        merge_into(st, m2, l2, o2);
+    }
+
+    // combine the 4 waves through LDS
+    __shared__ float red[kWaves][kPF];
+    if (lane < 16) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) red[w][2 + d0 + e] = st.o[e];
+        if (lane == 0) {
+            red[w][0] = st.m;
+            red[w][1] = st.l;
+        }
+    }
+    __syncthreads();
+    if (tid < kD) {
+        float mm = neg_inf();
+#pragma unroll
+        for (int k = 0; k < kWaves; ++k) mm = fmaxf(mm, red[k][0]);
+        const float mu = mm == neg_inf() ? 0.f : mm;
+        float l = 0.f, o = 0.f;
+#pragma unroll
+        for (int k = 0; k < kWaves; ++k) {
+            const float wk = exp2_hw(red[k][0] - mu);
+            l += wk * red[k][1];
+            o += wk * red[k][2 + tid];
+        }
+        float *dst = ws + (((size_t)s * H + h) * max_splits + split) * kPF;
+        dst[2 + tid] = o;
+        if (tid == 0) {
+            dst[0] = mm;
+            dst[1] = l;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kD) void decode_merge_kernel(
+    const float *__restrict__ ws, const int32_t *__restrict__ ctx_lens, uint16_t *__restrict__ o,
+    float *__restrict__ lse, int H, int max_splits)
+{
+    const int h = blockIdx.x;
+    const int s = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int ctx = ctx_lens[s];
+    const int n_pages = (ctx + kPS - 1) / kPS;
+    const int n_splits = (n_pages + kPPS - 1) / kPPS;
+    const float *src = ws + ((size_t)s * H + h) * max_splits * kPF;
+
+    float mm = neg_inf();
+    for (int k = 0; k < n_splits; ++k) mm = fmaxf(mm, src[k * kPF]);
+    const float mu = mm == neg_inf() ? 0.f : mm;
+    float l = 0.f, acc = 0.f;
+    for (int k = 0; k < n_splits; ++k) {
+        const float wk = exp2_hw(src[k * kPF] - mu);
+        l += wk * src[k * kPF + 1];
+        acc += wk * src[k * kPF + 2 + tid];
+    }
+    const float out = l > 0.f ? acc / l : 0.f;
+    o[((size_t)s * H + h) * kD + tid] = __builtin_bit_cast(uint16_t, (__bf16)out);
+    if (lse && tid == 0) lse[(size_t)s * H + h] = l > 0.f ? (mm + __log2f(l)) * kLn2 : neg_inf();
+}
+
+}  // namespace
+
+hipError_t launch_paged_decode(const void *q, const void *kcache, const void *vcache,
+                               const int32_t *block_table, const int32_t *ctx_lens, void *o,
+                               float *lse, int num_seqs, int H, int d, int page_size,
+                               int max_blocks_per_seq, float scale, float *workspace,
+                               hipStream_t stream)
+{
+    (void)d;
+    (void)page_size;
+    const int max_splits = decode_max_splits(max_blocks_per_seq);
+    const dim3 g1((unsigned)max_splits, (unsigned)H, (unsigned)num_seqs);
+    hipLaunchKernelGGL(decode_split_kernel, g1, dim3(256), 0, stream,
+                       static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(kcache),
+                       static_cast<const uint16_t *>(vcache), block_table, ctx_lens, workspace, H,
+                       max_blocks_per_seq, max_splits, scale * kLog2e);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const dim3 g2((unsigned)H, (unsigned)num_seqs);
+    hipLaunchKernelGGL(decode_merge_kernel, g2, dim3(kD), 0, stream, workspace, ctx_lens,
+                       static_cast<uint16_t *>(o), lse, H, max_splits);
+    return hipGetLastError();
+}
+
+}  // namespace fa

@@ -1,0 +1,37 @@
+// Internal launchers (host side). Arguments are already validated by the C ABI
+// layer; each launcher only computes the grid and enqueues kernels on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+hipError_t launch_fwd_f32(const float *q, const float *k, const float *v, float *o, float *lse,
+                          int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, void *o, float *lse,
+                           int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+hipError_t launch_fwd_fp8(const uint8_t *q8, const uint8_t *k8, const uint8_t *v8,
+                          const float *qs, const float *ks, const float *vs, void *o, float *lse,
+                          int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+// Pages per KV chunk (split) of the paged decode.
+constexpr int kDecodePagesPerSplit = 32;
+
+inline int decode_max_splits(int max_blocks_per_seq) {
+    return (max_blocks_per_seq + kDecodePagesPerSplit - 1) / kDecodePagesPerSplit;
+}
+
+// Floats per split partial: m, l, then d unscaled output values.
+inline size_t decode_partial_floats(int d) { return (size_t)d + 2; }
+
+hipError_t launch_paged_decode(const void *q, const void *kcache, const void *vcache,
+                               const int32_t *block_table, const int32_t *ctx_lens, void *o,
+                               float *lse, int num_seqs, int H, int d, int page_size,
+                               int max_blocks_per_seq, float scale, float *workspace,
+                               hipStream_t stream);
+
+}  // namespace fa

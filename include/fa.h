@@ -1,0 +1,126 @@
+/*
+ * fa.h - C ABI of the MI355X (gfx950) fused exact-attention library (libfa.so).
+ *
+ * The operation is exact attention O = softmax(scale * Q K^T [+ causal mask]) V
+ * with its per-row logsumexp L = m + ln(l), computed by a fused, tiled forward
+ * pass that never writes the N x N score or probability matrix to memory
+ * (the three steps and the single fused kernel: 91haoming.cn FlashAttention
+ * v1-v3 article, "FlashAttention v1 / attention implementation improvements";
+ * L kept instead of (m, l): same article, "FlashAttention v2 / forward pass
+ * improvements").
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are DEVICE pointers (HBM) unless stated otherwise; the caller
+ *     owns every buffer. The library allocates nothing and never synchronises:
+ *     all work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
+ *     the default stream), so results are ready once the stream is.
+ *   - Tensors are dense row-major: q/k/v/o [B, H, N, d], lse [B, H, N] fp32.
+ *   - Natural logarithms; L is in the units of the scaled scores.
+ *   - causal != 0: key j is visible to query i iff j <= i (top-left aligned,
+ *     diagonal visible; queries and keys have the same length N).
+ *   - Arguments are checked on the host before anything is launched. A failed
+ *     check returns its status and has no side effect. A launch failure
+ *     returns FA_ERR_HIP. Device-side contracts (block_table entries, ctx_lens)
+ *     are the caller's to keep and are not checked.
+ *   - Stateless and re-entrant; calls on different streams may overlap.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+    FA_OK = 0,
+    FA_ERR_NULL_PTR = 1,     /* a required pointer is NULL */
+    FA_ERR_BAD_SHAPE = 2,    /* a size is <= 0 or out of the supported range */
+    FA_ERR_UNSUPPORTED = 3,  /* head size / page size / flag value not supported */
+    FA_ERR_WORKSPACE = 4,    /* workspace too small */
+    FA_ERR_HIP = 5           /* the HIP runtime reported an error at launch */
+} fa_status;
+
+/*
+ * Fused attention forward, bf16 in / bf16 out (fp32 accumulation).
+ * q, k, v: bf16 [B, H, N, d]; o: bf16 [B, H, N, d] (rounded to nearest even);
+ * lse: fp32 [B, H, N] (may be NULL to skip it).
+ * d in {64, 128}; B, H, N >= 1 with B*H*N*d < 2^31.
+ * Tiling (row blocks of Q in parallel, K/V tiles streamed through on-chip
+ * memory, online softmax with one final 1/l): "FlashAttention系列优化",
+ * FlashAttentionV2 section and its equations.
+ */
+fa_status fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                 int B, int H, int N, int d, float scale, int causal, void *stream);
+
+/*
+ * Same operation in fp32 (fp32 in, fp32 out, fp32 arithmetic), any 1 <= d <= 128.
+ * The correctness path used for the worked example of "FlashAttention系列优化"
+ * (16 x 8, scale 1).
+ */
+fa_status fa_fwd_f32(const float *q, const float *k, const float *v, float *o, float *lse,
+                     int B, int H, int N, int d, float scale, int causal, void *stream);
+
+/*
+ * FP8 attention forward with per-block scales (FlashAttention-3 block
+ * quantisation: "FlashAttention系列优化", FlashAttentionV3 / FP低精度).
+ * q8, k8, v8: OCP E4M3FN bytes [B, H, N, d]; q_scale, k_scale, v_scale: fp32
+ * [B, H, ceil(N/128)], one per (batch, head, 128-token block); the value of an
+ * element is decode(x8) * scale of its block. o: bf16 [B, H, N, d];
+ * lse: fp32 [B, H, N] or NULL. d == 128. Q.K^T runs on fp8 MFMA; P.V runs on
+ * bf16 MFMA with V widened exactly from E4M3 to bf16.
+ */
+fa_status fa_fwd_fp8(const uint8_t *q8, const uint8_t *k8, const uint8_t *v8,
+                     const float *q_scale, const float *k_scale, const float *v_scale,
+                     void *o, float *lse, int B, int H, int N, int d,
+                     float scale, int causal, void *stream);
+
+/*
+ * Bytes of device workspace fa_paged_decode needs for these sizes (the split
+ * partials (m, l, unscaled O) of every (sequence, head, KV chunk)). Returns 0
+ * for unsupported sizes.
+ */
+size_t fa_paged_decode_workspace_bytes(int num_seqs, int H, int d, int page_size,
+                                       int max_blocks_per_seq);
+
+/*
+ * Decode attention over a paged KV cache (PagedAttention block table:
+ * "FlashAttention系列优化", PagedAttention section), one query token per
+ * sequence, split over KV chunks and merged with the same rescale identity as
+ * the FlashAttention-2 accumulator.
+ *   q:        bf16 [num_seqs, H, d]
+ *   kcache,
+ *   vcache:   bf16 [num_pages, H, page_size, d]; token t of sequence s lives in
+ *             page block_table[s][t / page_size], slot t % page_size
+ *   block_table: int32 [num_seqs, max_blocks_per_seq]; entries for the first
+ *             ceil(ctx_lens[s] / page_size) blocks must be in [0, num_pages);
+ *             the rest are ignored (pad with -1). Pages may be shared.
+ *   ctx_lens: int32 [num_seqs], each in [1, max_blocks_per_seq * page_size]
+ *             (0 gives O = 0 and L = -inf). Slots past the context in the last
+ *             page are never read.
+ *   o:        bf16 [num_seqs, H, d];  lse: fp32 [num_seqs, H] or NULL.
+ *   workspace: device memory of at least fa_paged_decode_workspace_bytes(...)
+ *             bytes; contents on entry do not matter.
+ * d == 128, page_size == 16. ctx_lens and block_table are read only on the
+ * device (no host synchronisation).
+ */
+fa_status fa_paged_decode(const void *q, const void *kcache, const void *vcache,
+                          const int32_t *block_table, const int32_t *ctx_lens,
+                          void *o, float *lse, int num_seqs, int H, int d,
+                          int page_size, int max_blocks_per_seq, int num_pages,
+                          float scale, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/* Human-readable name of a status (static string, never NULL). */
+const char *fa_status_str(fa_status s);
+
+/* Version of this ABI (major * 10000 + minor * 100 + patch). */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */
