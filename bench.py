@@ -64,12 +64,14 @@ def decode_bytes(p):
 
 def cpu_baseline(x, budget_s=15.0):
     """Time the fp64 oracle on a bounded sample of the causal prefill: query rows
-    i = 7 mod 8 of the first h heads, h chosen so the run takes about budget_s."""
+    i = stride-1 mod stride of the first h heads. A first head at stride 64 sets
+    the pace; the stride and head count are then chosen so that the whole
+    sample takes about budget_s."""
     import numpy as np
     import oracle
     B, H, N, d = x.q.shape
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
-    stride = 8
+    stride = 64
     rows = np.arange(stride - 1, N, stride)
 
     def head_f64(t, h):
@@ -87,14 +89,18 @@ def cpu_baseline(x, budget_s=15.0):
         return flops, t
 
     f1, t1 = run([0])
-    n_heads = max(1, min(H, int(budget_s / max(t1, 1e-3))))
-    f, t = run(list(range(1, n_heads + 1))[: H - 1] or [0])
-    f += f1
-    t += t1
-    n_used = 1 + min(n_heads, H - 1)
+    per_head = max(t1, 1e-3)                 # seconds per head at stride 64
+    n_heads = H - 1
+    while stride > 1 and per_head * 2 * n_heads <= budget_s:
+        stride //= 2
+        per_head *= 2
+    n_heads = max(1, min(H - 1, int(budget_s / per_head)))
+    rows = np.arange(stride - 1, N, stride)
+    f, t = run(list(range(1, n_heads + 1)))
     return {"value": f / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": "fp64 oracle, causal B1 H32 N16384 d128 rows i%%8==7 of %d heads "
-                      "(%d rows, %.3g flop, %.1f s)" % (n_used, n_used * len(rows), f, t)}
+            "sample": "fp64 oracle on causal B1 H32 N16384 d128 query rows i %% %d == %d of heads "
+                      "1..%d (%d rows, %.3g flop, %.1f s)" % (stride, stride - 1, n_heads,
+                                                            n_heads * len(rows), f, t)}
 
 
 def main():
@@ -105,6 +111,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--only", default="", help="comma list of prefill,fp8,decode (default all)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -168,6 +176,13 @@ def main():
     wall = time.perf_counter() - t0
     ms = {name: sum(a.elapsed_time(b) for a, b in ev[name]) / args.steps for name, _ in parts}
     log("mean ms per launch: %s" % ms)
+    if args.calib_copy_mib:
+        src = torch.ones(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copy of %d MiB done" % args.calib_copy_mib)
 
     result = {"metric": METRIC, "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
               "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True,

@@ -32,8 +32,35 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
-// Sum / max over the two halves (lanes l and l ^ 32) of a wave.
-__device__ __forceinline__ float xor32_sum(float x) { return x + __shfl_xor(x, 32); }
-__device__ __forceinline__ float xor32_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+// Value of lane l ^ 32 (the other half of the wave), without LDS: permlane32_swap
+// exchanges the upper half of its first operand with the lower half of its
+// second, so with both operands x the two results are x's lower and upper
+// halves broadcast to both halves.
+__device__ __forceinline__ float other_half_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float other_half_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Buffer resource over [base, base + bytes): loads past the end return zeros,
+// which is how tiles that run past N are padded without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+}
+
+// The running reference max of the online softmax only moves when a row's
+// tile max exceeds it by more than this (base-2 units); until then the terms
+// 2^(t - m) stay below 2^kRescaleSlack, and O~ and l are rescaled only when it
+// moves. The final O~/l and m + log2(l) are exact for any common reference.
+constexpr float kRescaleSlack = 8.0f;
 
 }  // namespace fa
