@@ -40,6 +40,31 @@ def prefill_flops(B, H, N, d, causal):
     return f / 2 if causal else f
 
 
+def measured_traffic(summary):
+    """HBM bytes per launch from a committed rocprofv3 counter summary
+    (profiles/<summary>), or None when the kernel sources it names have changed
+    since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", summary)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path, encoding="utf-8"):
+        if " = " in line and not line.startswith("|"):
+            key, val = line.strip().split(" = ", 1)
+            kv[key] = val
+    try:
+        h = hashlib.sha256()
+        for src in kv["sources"].split():
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != kv["source_sha256"]:
+            return None
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, OSError, ValueError):
+        return None
+
+
 def decode_bytes(p):
     """Algorithmic HBM bytes of one decode: every unique (page, head) slot of a
     valid token read once for K and once for V, plus q, O, L and the table
@@ -197,16 +222,18 @@ def main():
         tf = f / (ms["prefill"] * 1e-3) / 1e12
         result["value"] = tf
         result["roofline"] = {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS,
-                              "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS, "traffic": None,
-                              "kernel": "fwd_bf16_kernel<128,true>", "launch_ms": ms["prefill"],
+                              "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
+                              "traffic": measured_traffic("pmc_fwd_prefill_bf16_causal_B1H32N16384d128.md"),
+                              "kernel": "fwd_kernel<128,causal,bf16>", "launch_ms": ms["prefill"],
                               "flop_per_launch": f}
     if "fp8" in ms:
         f = prefill_flops(2, 16, 8192, 128, True)
         tf = f / (ms["fp8"] * 1e-3) / 1e12
         result["fp8"] = {"value": tf, "unit": "TFLOP/s", "launch_ms": ms["fp8"],
                          "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP8_TFLOPS,
-                                      "unit": "TFLOP/s", "frac": tf / PEAK_FP8_TFLOPS, "traffic": None,
-                                      "kernel": "fwd_fp8_kernel<true>"}}
+                                      "unit": "TFLOP/s", "frac": tf / PEAK_FP8_TFLOPS,
+                                      "traffic": measured_traffic("pmc_fwd_prefill_fp8_causal_B2H16N8192d128.md"),
+                                      "kernel": "fwd_kernel<128,causal,fp8>"}}
     if "decode" in ms:
         ub, lb = decode_bytes(p5)
         gbs = ub / (ms["decode"] * 1e-3) / 1e9
@@ -214,7 +241,8 @@ def main():
                             "bytes_unique": ub, "bytes_logical": lb,
                             "logical_GBps": lb / (ms["decode"] * 1e-3) / 1e9,
                             "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
-                                         "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "traffic": None,
+                                         "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                                         "traffic": measured_traffic("pmc_paged_decode_S64H32d128.md"),
                                          "kernel": "decode_split_kernel + decode_merge_kernel"}}
     if result["value"] is None and "decode" in result:
         result["value"], result["unit"] = result["decode"]["value"], "GB/s"
