@@ -224,7 +224,7 @@ def main():
         result["roofline"] = {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS,
                               "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
                               "traffic": measured_traffic("pmc_fwd_prefill_bf16_causal_B1H32N16384d128.md"),
-                              "kernel": "fwd_kernel<128,causal,bf16>", "launch_ms": ms["prefill"],
+                              "kernel": "fwd_kernel3<128,causal,bf16>", "launch_ms": ms["prefill"],
                               "flop_per_launch": f}
     if "fp8" in ms:
         f = prefill_flops(2, 16, 8192, 128, True)
@@ -233,7 +233,7 @@ def main():
                          "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP8_TFLOPS,
                                       "unit": "TFLOP/s", "frac": tf / PEAK_FP8_TFLOPS,
                                       "traffic": measured_traffic("pmc_fwd_prefill_fp8_causal_B2H16N8192d128.md"),
-                                      "kernel": "fwd_kernel<128,causal,fp8>"}}
+                                      "kernel": "fwd_kernel3<128,causal,fp8>"}}
     if "decode" in ms:
         ub, lb = decode_bytes(p5)
         gbs = ub / (ms["decode"] * 1e-3) / 1e9

@@ -7,40 +7,42 @@
 //   * one workgroup per (batch*head, row block of 256 queries), no
 //     communication between workgroups; causal grids are issued heaviest row
 //     block first;
-//   * 8 waves per workgroup (two per SIMD), each owning 32 query rows
-//     (split-Q);
-//   * K/V tiles of 64 keys stream through a 4-stage LDS ring, three tiles
-//     ahead of the compute, by buffer loads that write LDS directly (no
-//     register staging). LDS rows are dense; 16-byte chunks are XOR-swizzled by
-//     row so that both the MFMA operand reads of K and the transpose reads of
-//     V are free of bank conflicts.
+//   * 4 waves per workgroup, one per SIMD with the whole register file; a
+//     wave owns 64 query rows as two groups of 32 (split-Q), and every K or V
+//     fragment it reads from LDS feeds the MFMAs of both groups;
+//   * K and V tiles of 64 keys stream through LDS rings (3 K tiles, 4 V
+//     tiles) by buffer loads that write LDS directly, two tiles ahead of the
+//     compute. LDS rows are dense; 16-byte chunks are XOR-swizzled by row so
+//     that both the MFMA operand reads of K and the transpose reads of V are
+//     free of bank conflicts.
 //
-// MFMA orientation. Each wave computes S^T = K_j Q_i^T (A = 32 keys x 16
-// channels from LDS, B = the wave's 32 queries held in registers). In the
-// 32x32 accumulator layout a lane holds one query and 16 keys, so the row max
-// and sum of the online softmax are in-lane reductions plus one exchange
-// between the wave halves (v_permlane32_swap). The same registers, rounded to
-// bf16, are directly the B operand of O^T += V_j^T P^T. V stays row-major in
-// LDS and the A operand V^T is read with ds_read_b64_tr_b16, whose lane
-// transpose delivers 4 keys of one channel per lane; the keys a lane reads are
-// the ones its P registers hold (keys are a summation index, so only the
-// pairing matters).
+// MFMA orientation. S^T = K_j Q_i^T (A = 32 keys x 16 channels from LDS,
+// B = 32 queries in AGPRs). In the 32x32 accumulator layout a lane holds one
+// query and 16 keys, so the row max and sum of the online softmax are in-lane
+// reductions plus one exchange between the wave halves (v_permlane32_swap).
+// The same values, rounded to bf16, are directly the B operand of
+// O^T += V_j^T P^T. V stays row-major in LDS and the A operand V^T is read with
+// ds_read_b64_tr_b16, whose lane transpose delivers 4 keys of one channel per
+// lane; the keys a lane reads are the ones its P registers hold (keys are a
+// summation index, so only the pairing matters).
 //
 // Online softmax (pseudocode of the FlashAttentionV1 section and the V2
 // equations of "FlashAttention系列优化"): running reference max m, unscaled
 // sums, unscaled O accumulator, one final division, L = (m + log2 l) ln 2, in
 // base 2 (t = s * scale * log2 e). The reference max only moves when a row max
-// exceeds it by more than kRescaleSlack. O is divided by the sum of the
-// bf16-rounded weights that the P.V MFMA actually used; L uses the fp32 sum.
+// exceeds it by more than kRescaleSlack, so O is rarely rescaled. The
+// softmax of a tile overlaps the MFMAs of its neighbours (P.V of the previous
+// tile, Q.K of the next), the ping-pong of the FlashAttentionV3 section of the
+// same page done inside one wave.
 //
 // FP8 (FlashAttention-3 block quantisation, "FlashAttention系列优化",
 // FlashAttentionV3 / FP低精度): S^T = K8 Q8^T on v_mfma_f32_32x32x16_fp8_fp8
-// (products of E4M3 values are exact); row blocks (128) coincide with the
-// scale blocks and a 64-key tile lies in one scale block, so dequantisation is
-// one scalar per tile folded into the softmax multiplier. V is widened
-// E4M3 -> bf16 (exact) on its way into LDS and P.V runs on bf16 MFMA with the
-// tile's V scale folded into P. P is not quantised to E4M3: with V outliers of
-// tens, a 3-bit mantissa on P would exceed this path's accuracy bound.
+// (products of E4M3 values are exact); a 64-key tile lies in one 128-row scale
+// block, so dequantisation is one scalar per tile folded into the softmax
+// multiplier. V is widened E4M3 -> bf16 (exact) on its way into LDS and P.V
+// runs on bf16 MFMA with the tile's V scale folded into P. P is not quantised
+// to E4M3: with V outliers of tens, a 3-bit mantissa on P would exceed this
+// path's accuracy bound.
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -51,29 +53,10 @@ namespace {
 
 constexpr int kBR = 256;       // query rows per workgroup
 constexpr int kBC = 64;        // keys per tile
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kStages = 4;     // LDS ring depth; tiles are fetched kStages - 1 ahead
 constexpr int kScaleBlock = 128;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-template <int D, bool FP8>
-struct Layout {
-    static constexpr int KROW = FP8 ? D : 2 * D;   // bytes of a K (and HBM V) row
-    static constexpr int VROW = 2 * D;             // bytes of a V row in LDS (bf16)
-    static constexpr int K_TILE = kBC * KROW;
-    static constexpr int V_TILE = kBC * VROW;
-    static constexpr int STAGE = K_TILE + V_TILE;
-    static constexpr int K_DMA = K_TILE / 1024 / kWaves;   // 1 KiB direct loads per wave per tile
-    static constexpr int V_DMA = FP8 ? 0 : V_TILE / 1024 / kWaves;
-    static constexpr int DMA = K_DMA + V_DMA;
-    static constexpr int V8_LOADS = FP8 ? kBC * D / 16 / kThreads : 0;   // 16-byte E4M3 chunks per thread
-};
-
-// XOR swizzle of the 16-byte chunks of LDS row r (cpr chunks per row). With it,
-// 16 rows read at one logical chunk land on 16 different chunk positions, and
-// 8 consecutive rows read at four consecutive chunks cover every bank twice.
 template <int CPR>
 __device__ __forceinline__ int swz(int r) {
     if constexpr (CPR == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
@@ -84,11 +67,6 @@ __device__ __forceinline__ int swz(int r) {
 __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w, bool hi) {
     const f32x2 f = hi ? __builtin_amdgcn_cvt_pk_f32_fp8(w, true) : __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
     return (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xffff0000u);
-}
-
-__device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t *p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (s16x4 __attribute__((address_space(3))) *)(const_cast<uint8_t *>(p)));
 }
 
 // Plain buffer descriptor (base, no stride, num_records = bytes, raw access):
@@ -149,16 +127,144 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// ---------------------------------------------------------------------------
+// Hand-scheduled kernel: 4 waves x 64 queries (two 32-query groups g0, g1 per
+// wave), one wave per SIMD. Every K or V fragment read from LDS feeds the MFMA
+// of both groups. A block is a fixed sequence of slots; a slot holds at most
+// one MFMA, the LDS reads that run a few MFMAs ahead, an exact lgkmcnt wait,
+// and a fixed share of the softmax VALU work:
+//
+//   block j:  slots [0, NS_PV):  O(g) += V_{j-1}^T P_{j-1}^T(g)   | max of S_j, reference
+//                                                                 | move, weights of keys 0..31
+//             slots [NS_PV, NS): S_{j+1}(g) = K_{j+1} Q_g^T        | weights of keys 32..63
+//
+// MFMAs and LDS reads are inline asm so that their order, the registers they
+// use (S and P in VGPRs, O and Q in AGPRs) and the waits are fixed here; the
+// compiler only places the VALU work inside each slot. Register hazards the
+// compiler cannot see are avoided by distance: S written by a block is read
+// in the next one, P written in a block is read in the next one, P of the
+// previous tile is overwritten only slots after its last MFMA read, and the
+// only AGPR writes (rescale) sit between blocks.
+//
+// K has a ring of 3 tiles and V of 4. Block j (or the idle step j of a wave
+// that is done) issues the copies of V(j+2) and K(j+3); the step before block
+// j waits for V(j) and K(j+1). V(j) is read at the end of block j to prefetch
+// the first fragments of the next block. fp8 V is staged through registers
+// (loaded in block j-1, converted to bf16 and stored before block j).
+constexpr int kThreads3 = 256;
+constexpr int kKRing = 3;
+constexpr int kVRing = 4;
+
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+template <int OFF> __device__ __forceinline__ u32x4 ds_b128(uint32_t a) {
+    u32x4 r;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(a), "n"(OFF));
+    return r;
+}
+template <int OFF> __device__ __forceinline__ u32x2 ds_b64(uint32_t a) {
+    u32x2 r;
+    asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(r) : "v"(a), "n"(OFF));
+    return r;
+}
+template <int OFF> __device__ __forceinline__ u32x2 ds_tr16(uint32_t a) {
+    u32x2 r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(a), "n"(OFF));
+    return r;
+}
+template <int N> __device__ __forceinline__ void wait_lgkm() {
+    static_assert(N >= 0 && N < 16, "lgkmcnt range");
+    asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N));
+}
+// S (VGPR) = / += A (VGPR) x B (AGPR)
+__device__ __forceinline__ void mfma_s_first(f32x16 &s, u32x4 a, u32x4 b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_s(f32x16 &s, u32x4 a, u32x4 b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_s_first(f32x16 &s, u32x2 a, u32x2 b) {
+    asm volatile("v_mfma_f32_32x32x16_fp8_fp8 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_s(f32x16 &s, u32x2 a, u32x2 b) {
+    asm volatile("v_mfma_f32_32x32x16_fp8_fp8 %0, %1, %2, %0" : "+v"(s) : "v"(a), "a"(b));
+}
+// O (AGPR) += A (VGPR) x B (VGPR)
+__device__ __forceinline__ void mfma_o(f32x16 &o, u32x4 a, u32x4 b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(a), "v"(b));
+}
+
+// LDS reads taken by fragment f of a block (0 if it does not exist)
+template <int NFV, int NFK, bool HAS_PV, bool HAS_QK, bool PREF>
+constexpr int frag_reads(int f) {
+    return f < NFV ? (HAS_PV ? 2 : 0) : f < NFV + NFK ? (HAS_QK ? 1 : 0) : (PREF ? 2 : 0);
+}
+template <int NFV, int NFK, bool HAS_PV, bool HAS_QK, bool PREF>
+constexpr int reads_between(int a, int b) {
+    int c = 0;
+    for (int f = a; f <= b; ++f) c += frag_reads<NFV, NFK, HAS_PV, HAS_QK, PREF>(f);
+    return c;
+}
+// fragment f is read in slot 2 (f - PRE); fragments below PRE come from the step before
+template <int PRE>
+constexpr int frag_issue_slot(int f) { return 2 * (f - PRE) < 0 ? 0 : 2 * (f - PRE); }
+
+// softmax element e (0..31) of a block: its fma slot, for keys 0..31 (part 1)
+// and keys 32..63 (part 2); e_first(s) is the first element whose slot is >= s
+template <int S0, int W>
+constexpr int elem_slot(int e) { return S0 + (e * W) / 32; }
+template <int S0, int W>
+constexpr int elem_first(int s) {
+    int e = 0;
+    while (e < 32 && elem_slot<S0, W>(e) < s) ++e;
+    return e;
+}
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
+template <int D, bool FP8>
+struct Layout3 {
+    static constexpr int KROW = FP8 ? D : 2 * D;
+    static constexpr int VROW = 2 * D;
+    static constexpr int K_TILE = kBC * KROW;
+    static constexpr int V_TILE = kBC * VROW;
+    static constexpr int K_DMA = K_TILE / 1024 / 4;                 // 1 KiB copies per wave
+    static constexpr int V_DMA = FP8 ? 0 : V_TILE / 1024 / 4;
+    static constexpr int V8_LOADS = FP8 ? kBC * D / 16 / kThreads3 : 0;
+    static constexpr int LDS = kKRing * K_TILE + kVRing * V_TILE;
+    static constexpr int KC = D / 16;        // QK k-steps
+    static constexpr int DT = D / 32;        // PV output tiles
+    static constexpr int NFV = 4 * DT;       // PV fragments (f = ch * DT + t)
+    static constexpr int NFK = 2 * KC;       // QK fragments (f = kt * KC + kc)
+    static constexpr int NS_PV = 2 * NFV;    // PV slots
+    static constexpr int NS_QK = 2 * NFK;    // QK slots
+    static constexpr int NS = NS_PV + NS_QK;
+    static constexpr int PRE = 4;            // fragments read ahead
+    static constexpr int MX = NS_PV / 4;     // slots of the row max
+};
+
 template <int D, bool CAUSAL, bool FP8>
-__global__ __launch_bounds__(kThreads, 1) void fwd_kernel(
+__global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
     const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K, const uint8_t *__restrict__ V,
     const float *__restrict__ QS, const float *__restrict__ KSc, const float *__restrict__ VSc,
     uint16_t *__restrict__ O, float *__restrict__ LSE, int N, int BH, int n_rb, float c0)
 {
-    using L = Layout<D, FP8>;
+    using L = Layout3<D, FP8>;
     constexpr int KCPR = L::KROW / 16;
     constexpr int VCPR = L::VROW / 16;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * L::STAGE];
+    constexpr int KC = L::KC, DT = L::DT, NFV = L::NFV, NFK = L::NFK;
+    constexpr int NS_PV = L::NS_PV, NS_QK = L::NS_QK, NS = L::NS, PRE = L::PRE, MX = L::MX;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[L::LDS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -171,47 +277,52 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(
     const int rb = CAUSAL ? (n_rb - 1 - rank) : rank;
     const size_t head_off = (size_t)bh * N * L::KROW;
     const uint32_t head_bytes = (uint32_t)N * L::KROW;
-    // loads past row N - 1 of this head return zeros
     const u32x4 rq = sgpr_rsrc(Q + head_off, head_bytes);
     const u32x4 rk = sgpr_rsrc(K + head_off, head_bytes);
     const u32x4 rv = sgpr_rsrc(V + head_off, head_bytes);
 
     const int q0 = rb * kBR;
-    const int qw = q0 + w * 32;
-    const int my_q = qw + l32;
+    const int qw = q0 + w * 64;
+    const int my_q[2] = {qw + l32, qw + 32 + l32};
 
-    float c = c0;
+    float cg[2] = {c0, c0};
     const float *ks_h = nullptr, *vs_h = nullptr;
     if constexpr (FP8) {
         const int nsb = (N + kScaleBlock - 1) / kScaleBlock;
-        // a wave's 32 queries lie in one 128-token scale block (clamped for padding rows)
-        c = c0 * QS[(size_t)bh * nsb + min(qw / kScaleBlock, nsb - 1)];
+        const float *qs_h = QS + (size_t)bh * nsb;
+        cg[0] = c0 * qs_h[min(qw / kScaleBlock, nsb - 1)];
+        cg[1] = c0 * qs_h[min((qw + 32) / kScaleBlock, nsb - 1)];
         ks_h = KSc + (size_t)bh * nsb;
         vs_h = VSc + (size_t)bh * nsb;
     }
 
-    // Q fragments: B operand, lane (query l32, channel group hf) of each 16-channel
-    // chunk; loaded first, waited for after the prologue copies are issued
-    typedef typename std::conditional<FP8, u32x2, u32x4>::type QRaw;
-    QRaw qraw[D / 16];
+    // Q fragments of both groups (B operand of S = K Q^T)
+    typedef typename std::conditional<FP8, u32x2, u32x4>::type QF;
+    QF qa[2][KC];
 #pragma unroll
-    for (int kc = 0; kc < D / 16; ++kc) {
-        if constexpr (FP8)
-            qraw[kc] = vload8(rq, (uint32_t)(my_q * D + 16 * kc + 8 * hf), 0);
-        else
-            qraw[kc] = vload16(rq, (uint32_t)(my_q * D + 16 * kc + 8 * hf) * 2, 0);
-    }
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+            if constexpr (FP8)
+                qa[g][kc] = vload8(rq, (uint32_t)(my_q[g] * D + 16 * kc + 8 * hf), 0);
+            else
+                qa[g][kc] = vload16(rq, (uint32_t)(my_q[g] * D + 16 * kc + 8 * hf) * 2, 0);
+        }
 
     const int kend = CAUSAL ? min(N, q0 + kBR) : N;
     const int n_tiles = (kend + kBC - 1) / kBC;
-    // tiles this wave computes: a prefix 0 .. last (causal waves stop at their diagonal)
-    const int last = CAUSAL ? min(n_tiles - 1, (qw + 31) / kBC) : n_tiles - 1;
+    // last tile of this wave; for causal the diagonal one (qw is a multiple of
+    // 64, so both groups end on it)
+    const int last = CAUSAL ? min(n_tiles - 1, qw / kBC) : n_tiles - 1;
+    // tiles below j_mask are fully visible to the wave's 64 queries; only
+    // `last` can be at or above it
+    const int j_mask = min(CAUSAL ? last : n_tiles, N / kBC);
 
-    // direct-load source offsets (within a tile) of this lane, for its wave's 1 KiB blocks
+    // ---- copies (tiles past the end read zeros into a free stage) ----
     uint32_t kdma_off[L::K_DMA];
 #pragma unroll
     for (int i = 0; i < L::K_DMA; ++i) {
-        const int pos = (w * L::K_DMA + i) * 64 + lane;   // 16-byte chunk position in the tile
+        const int pos = (w * L::K_DMA + i) * 64 + lane;
         const int r = pos / KCPR, pc = pos % KCPR;
         kdma_off[i] = (uint32_t)(r * L::KROW + ((pc ^ swz<KCPR>(r)) << 4));
     }
@@ -222,35 +333,36 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(
         const int r = pos / VCPR, pc = pos % VCPR;
         vdma_off[i] = (uint32_t)(r * L::VROW + ((pc ^ swz<VCPR>(r)) << 4));
     }
-    const uint32_t lds_base = (uint32_t)(size_t)smem;
-    auto issue_tile = [&](int j) {
-        const uint32_t sk = lds_base + (j % kStages) * L::STAGE;
-        const uint32_t soff = (uint32_t)(j * kBC) * L::KROW;
-#pragma unroll
-        for (int i = 0; i < L::K_DMA; ++i) dma16(rk, sk + (w * L::K_DMA + i) * 1024, kdma_off[i], soff);
-#pragma unroll
-        for (int i = 0; i < L::V_DMA; ++i) dma16(rv, sk + L::K_TILE + (w * L::V_DMA + i) * 1024, vdma_off[i], soff);
+    const uint32_t lds_k = (uint32_t)(size_t)smem;
+    const uint32_t lds_v = lds_k + kKRing * L::K_TILE;
+    auto issue_k_part = [&](int j, int i) {
+        const uint32_t dst = lds_k + (uint32_t)(j % kKRing) * L::K_TILE + (w * L::K_DMA + i) * 1024;
+        dma16(rk, dst, kdma_off[i], (uint32_t)(j * kBC) * L::KROW);
     };
-    // FP8 V: E4M3 chunks through registers, widened to bf16 into the swizzled V tile
     u32x4 v8reg[L::V8_LOADS > 0 ? L::V8_LOADS : 1];
-    auto load_v8 = [&](int j) {
-        const uint32_t base = (uint32_t)(j * kBC) * L::KROW;
-#pragma unroll
-        for (int i = 0; i < L::V8_LOADS; ++i) v8reg[i] = vload16(rv, (uint32_t)(tid + i * kThreads) * 16, base);
+    auto issue_v_part = [&](int j, int i) {
+        const uint32_t soff = (uint32_t)(j * kBC) * L::KROW;
+        if constexpr (FP8) {
+            v8reg[i] = vload16(rv, (uint32_t)(tid + i * kThreads3) * 16, soff);
+        } else {
+            const uint32_t dst = lds_v + (uint32_t)(j & (kVRing - 1)) * L::V_TILE + (w * L::V_DMA + i) * 1024;
+            dma16(rv, dst, vdma_off[i], soff);
+        }
     };
-    // wait for the E4M3 registers (at most n later copies still in flight); the
-    // registers pass through the asm so no use can be scheduled before the wait
-    auto wait_v8 = [&](int n) {
-        wait_vm(n);
-#pragma unroll
-        for (int i = 0; i < L::V8_LOADS; ++i) asm volatile("" : "+v"(v8reg[i]));
+    constexpr int NV_ISSUE = FP8 ? L::V8_LOADS : L::V_DMA;
+    constexpr int N_ISSUE = NV_ISSUE + L::K_DMA;
+    // the copies of step j: V first (fp8: V(j+1) into registers; bf16: V(j+2)), then K(j+3)
+    auto issue_part = [&](int j, int i) {
+        if (i < NV_ISSUE) issue_v_part(FP8 ? j + 1 : j + 2, i);
+        else issue_k_part(j + 3, i - NV_ISSUE);
     };
     auto store_v8 = [&](int j) {
-        uint8_t *sv = smem + (j % kStages) * L::STAGE + L::K_TILE;
+        uint8_t *sv = smem + kKRing * L::K_TILE + (j & (kVRing - 1)) * L::V_TILE;
 #pragma unroll
         for (int i = 0; i < L::V8_LOADS; ++i) {
-            const int idx = tid + i * kThreads;
-            const int r = idx / (D / 16), c8 = idx % (D / 16);   // 16 E4M3 channels = bf16 chunks 2c8, 2c8+1
+            asm volatile("" : "+v"(v8reg[i]));
+            const int idx = tid + i * kThreads3;
+            const int r = idx / (D / 16), c8 = idx % (D / 16);
             u32x4 lo, hi;
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
@@ -264,197 +376,358 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(
         }
     };
 
-    // operand-read offsets of this lane (row bits below 16 are the lane's, so the
-    // swizzle is a per-lane constant for each logical chunk)
-    uint32_t koff[D / 16];
+    // ---- operand-read offsets of this lane ----
+    uint32_t koff[KC];
 #pragma unroll
-    for (int kc = 0; kc < D / 16; ++kc) {
+    for (int kc = 0; kc < KC; ++kc) {
         if constexpr (FP8)
             koff[kc] = (uint32_t)(l32 * L::KROW + ((kc ^ swz<KCPR>(l32)) << 4) + 8 * hf);
         else
             koff[kc] = (uint32_t)(l32 * L::KROW + (((2 * kc + hf) ^ swz<KCPR>(l32)) << 4));
     }
-    // transpose reads: 16-lane group G supplies 4 keys x 16 channels; lane s = 4e + j
-    // of the group points at key 4 (G/2) + e (+ 8 rd), channels 16 (G%2) + 4 j .. +3 (+ 32 t)
     const int tr_G = lane >> 4, tr_e = (lane & 15) >> 2, tr_j = lane & 3;
-    uint32_t voff[2][D / 32];
+    uint32_t voff[2][DT];
 #pragma unroll
     for (int rd = 0; rd < 2; ++rd)
 #pragma unroll
-        for (int t = 0; t < D / 32; ++t) {
+        for (int t = 0; t < DT; ++t) {
             const int r = 8 * rd + 4 * (tr_G >> 1) + tr_e;
             const int cidx = 4 * t + 2 * (tr_G & 1) + (tr_j >> 1);
             voff[rd][t] = (uint32_t)(r * L::VROW + ((cidx ^ swz<VCPR>(r)) << 4) + 8 * (tr_j & 1));
         }
 
-    f32x16 oacc[D / 32];
+    typedef typename std::conditional<FP8, u32x2, u32x4>::type KF;
+    f32x16 oacc[2][DT];
+    f32x16 sacc[2][2];          // S^T of the newest tile (VGPR)
+    bf16x8 pf[2][4];            // P^T of the tile the next PV consumes
+    u32x2 pre_lo[PRE], pre_hi[PRE];   // V fragments read ahead for the next block
+    float m[2] = {neg_inf(), neg_inf()};
+    float lsum[2] = {0.f, 0.f};
+    float alpha[2] = {1.f, 1.f};
+    bool moved[2] = {false, false};
+    float ctj[2] = {cg[0], cg[1]};   // scale (and log2 e) of the current tile
+    float psj = 1.f;                 // V dequant scale of the current tile
 #pragma unroll
-    for (int t = 0; t < D / 32; ++t) oacc[t] = f32x16{};
-    float m = neg_inf();  // reference max (base 2), moved only by more than kRescaleSlack
-    float lsum = 0.f;     // this lane's share of l (fp32 weights)
-    float lsumb = 0.f;    // same, over the bf16-rounded weights the P.V product uses
-
-    // zero the ring once: rows past N of a partial tile then hold zeros or
-    // earlier finite values, never uninitialised bits (their weights are 0)
-    for (int i = tid; i < kStages * L::STAGE / 16; i += kThreads)
-        reinterpret_cast<u32x4 *>(smem)[i] = u32x4{};
-    lds_barrier();
-
-    // prologue: tiles 0 .. kStages-2 in flight
-    const int pro = min(n_tiles, kStages - 1);
-    if constexpr (FP8) load_v8(0);
-    for (int jj = 0; jj < pro; ++jj) issue_tile(jj);
-    // Q (issued before everything else) has landed once at most the copies and
-    // E4M3 loads issued after it are outstanding
-    wait_vm(pro * L::DMA + (FP8 ? L::V8_LOADS : 0));
-    typedef typename std::conditional<FP8, long, bf16x8>::type QFrag;
-    QFrag qf[D / 16];
+    for (int g = 0; g < 2; ++g)
 #pragma unroll
-    for (int kc = 0; kc < D / 16; ++kc) {
-        asm volatile("" : "+v"(qraw[kc]));
-        qf[kc] = __builtin_bit_cast(QFrag, qraw[kc]);
-    }
-    if constexpr (FP8) {
-        wait_v8((pro - 1) * L::DMA);   // the E4M3 registers and tile 0 (issued before tiles 1..)
-        store_v8(0);
-    } else {
-        wait_vm((pro - 1) * L::DMA);
-    }
-    lds_barrier();
+        for (int t = 0; t < DT; ++t) oacc[g][t] = f32x16{};
 
-    for (int j = 0; j < n_tiles; ++j) {
-        const int st = j % kStages;
-        const bool next_v8 = FP8 && j + 1 < n_tiles;
-        if constexpr (FP8)
-            if (next_v8) load_v8(j + 1);
-        const bool ahead = j + kStages - 1 < n_tiles;
-        if (ahead) issue_tile(j + kStages - 1);
-        if (j <= last) {
-            const int k0 = j * kBC;
-            const uint8_t *sk = smem + st * L::STAGE;
-            const uint8_t *sv = sk + L::K_TILE;
-            float ct = c, pscale = 1.f, inv_pscale = 1.f;
-            if constexpr (FP8) {
-                ct = c * ks_h[k0 / kScaleBlock];
-                pscale = vs_h[k0 / kScaleBlock];
-                inv_pscale = 1.f / pscale;
-            }
-
-            // S^T = K_j Q^T : two 32-key sub-tiles
-            f32x16 sacc[2];
+    // One block. HAS_PV: O += V_{j-1}^T P^T; HAS_QK: S = K_{j+1} Q^T;
+    // HAS_SM: softmax of tile j; PREF: read the first V_j fragments for the
+    // next PV; ISSUE: the copies of step j.
+    auto block = [&](int j, bool masked, auto has_pv_c, auto has_qk_c, auto has_sm_c, auto pref_c,
+                     auto issue_c) {
+        constexpr bool HAS_PV = decltype(has_pv_c)::value;
+        constexpr bool HAS_QK = decltype(has_qk_c)::value;
+        constexpr bool HAS_SM = decltype(has_sm_c)::value;
+        constexpr bool PREF = decltype(pref_c)::value;
+        constexpr bool ISSUE = decltype(issue_c)::value;
+        constexpr int NF = NFV + NFK + PRE;
+        uint32_t ka[KC], va[2][DT], vn[2][DT];
+        if constexpr (HAS_QK) {
+            const uint32_t kb = __builtin_amdgcn_readfirstlane(lds_k + (uint32_t)((j + 1) % kKRing) * L::K_TILE);
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                sacc[kt] = f32x16{};
+            for (int kc = 0; kc < KC; ++kc) ka[kc] = kb + koff[kc];
+        }
+        if constexpr (HAS_PV) {
+            const uint32_t vb = __builtin_amdgcn_readfirstlane(lds_v + (uint32_t)((j - 1) & (kVRing - 1)) * L::V_TILE);
 #pragma unroll
-                for (int kc = 0; kc < D / 16; ++kc) {
-                    if constexpr (FP8) {
-                        const long a = *reinterpret_cast<const long *>(sk + kt * 32 * L::KROW + koff[kc]);
-                        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a, qf[kc], sacc[kt], 0, 0, 0);
-                    } else {
-                        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(sk + kt * 32 * L::KROW + koff[kc]);
-                        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], sacc[kt], 0, 0, 0);
-                    }
+            for (int rd = 0; rd < 2; ++rd)
+#pragma unroll
+                for (int t = 0; t < DT; ++t) va[rd][t] = vb + voff[rd][t];
+        }
+        if constexpr (PREF) {
+            const uint32_t vb = __builtin_amdgcn_readfirstlane(lds_v + (uint32_t)(j & (kVRing - 1)) * L::V_TILE);
+#pragma unroll
+            for (int rd = 0; rd < 2; ++rd)
+#pragma unroll
+                for (int t = 0; t < DT; ++t) vn[rd][t] = vb + voff[rd][t];
+        }
+        u32x2 vlo[NFV], vhi[NFV];
+        KF kfr[NFK];
+        u32x2 nlo[PRE], nhi[PRE];
+        auto read = [&](auto fc) {
+            constexpr int f = decltype(fc)::value;
+            if constexpr (f < NFV) {
+                if constexpr (HAS_PV && f >= PRE) {
+                    constexpr int ch = f / DT, t = f % DT;
+                    vlo[f] = ds_tr16<16 * ch * L::VROW>(va[0][t]);
+                    vhi[f] = ds_tr16<16 * ch * L::VROW>(va[1][t]);
+                }
+            } else if constexpr (f < NFV + NFK) {
+                if constexpr (HAS_QK) {
+                    constexpr int q = f - NFV, kt = q / KC, kc = q % KC;
+                    if constexpr (FP8) kfr[q] = ds_b64<kt * 32 * L::KROW>(ka[kc]);
+                    else kfr[q] = ds_b128<kt * 32 * L::KROW>(ka[kc]);
+                }
+            } else {
+                if constexpr (PREF) {
+                    constexpr int p = f - NFV - NFK, ch = p / DT, t = p % DT;
+                    nlo[p] = ds_tr16<16 * ch * L::VROW>(vn[0][t]);
+                    nhi[p] = ds_tr16<16 * ch * L::VROW>(vn[1][t]);
                 }
             }
+        };
 
-            // mask keys past N and (causal) keys after the query: register i of
-            // sub-tile kt holds key k0 + 4 hf + kt*32 + 8 (i/4) + i%4
-            const bool need_mask = (k0 + kBC > N) || (CAUSAL && k0 + kBC - 1 > qw);
-            if (need_mask) {
-                const int lim = (CAUSAL ? min(my_q, N - 1) : N - 1) - (k0 + 4 * hf);
+        // softmax state of this block
+        float mx[2] = {neg_inf(), neg_inf()};
+        float mu[2] = {0.f, 0.f};
+        float x[2][2][16];
+        float rsum[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+        // S was written by the MFMAs at the end of the previous block: cover
+        // the MFMA-write -> VALU-access distance before the softmax touches it
+        if constexpr (HAS_SM) asm volatile("s_nop 7\n\ts_nop 7");
+        if (HAS_SM && masked) {
+            const int k0 = j * kBC;
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                const int lim = (CAUSAL ? min(qw + 32 * g + l32, N - 1) : N - 1) - (k0 + 4 * hf);
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                     for (int i = 0; i < 16; ++i)
-                        if (kt * 32 + 8 * (i >> 2) + (i & 3) > lim) sacc[kt][i] = neg_inf();
+                        if (kt * 32 + 8 * (i >> 2) + (i & 3) > lim) sacc[g][kt][i] = neg_inf();
             }
-
-            // online softmax (base 2) with a lazily moved reference max
-            float mx = neg_inf();
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kt][i]);
-            const float mxc = other_half_max(mx) * ct;
-            const bool move = mxc > m + kRescaleSlack;
-            if (__builtin_amdgcn_ballot_w64(move)) {
-                const float m_new = move ? mxc : m;
-                const float alpha = exp2_hw(m - m_new);
-                lsum *= alpha;
-                lsumb *= alpha;
-#pragma unroll
-                for (int t = 0; t < D / 32; ++t) oacc[t] *= alpha;
-                m = m_new;
-            }
-            const float m_use = m == neg_inf() ? 0.f : m;
-
-            float rs = 0.f, rsb = 0.f;
-            bf16x8 pf[4];
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float p = exp2_hw(fmaf(sacc[kt][i], ct, -m_use));
-                    rs += p;
-                    pf[kt * 2 + (i >> 3)][i & 7] = (__bf16)(FP8 ? p * pscale : p);
-                }
-            typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-            const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-            for (int ch = 0; ch < 4; ++ch) {
-                rsb = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[ch], pf[ch], 0, 1), ones, rsb, false);
-                rsb = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[ch], pf[ch], 2, 3), ones, rsb, false);
-                rsb = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[ch], pf[ch], 4, 5), ones, rsb, false);
-                rsb = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[ch], pf[ch], 6, 7), ones, rsb, false);
-            }
-            lsum += rs;
-            lsumb = FP8 ? fmaf(rsb, inv_pscale, lsumb) : lsumb + rsb;
-
-            // O^T += V^T P^T : 16-key chunks; A operand = two transpose reads
-            // (keys 16ch + 4 hf + 0..3 and 16ch + 8 + 4 hf + 0..3)
-#pragma unroll
-            for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-                for (int ch = 0; ch < 4; ++ch) {
-                    const uint8_t *p0 = sv + 16 * ch * L::VROW;
-                    const s16x4 lo = lds_read_tr16(p0 + voff[0][t]);
-                    const s16x4 hi = lds_read_tr16(p0 + voff[1][t]);
-                    const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                    oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ch], oacc[t], 0, 0, 0);
-                }
         }
 
-        // tile j+1 must have landed: the copies of tiles j+2 .. j+kStages-1 may
-        // still be in flight (the E4M3 loads of tile j+1 were issued before tile
-        // j+kStages-1's copies, so the same count covers them)
-        const int in_flight = (min(n_tiles - 1, j + kStages - 1) - min(n_tiles - 1, j + 1)) * L::DMA;
+        static_for<NS>([&](auto sc) {
+            constexpr int s = decltype(sc)::value;
+            // 1. LDS reads issued in this slot
+            if constexpr (s % 2 == 0 && s / 2 + PRE < NF) read(std::integral_constant<int, s / 2 + PRE>{});
+            // 2./3. wait for this slot's fragment, then its MFMA
+            constexpr int n = s / 2, g = s % 2;
+            constexpr bool mf = s < NS_PV ? HAS_PV : HAS_QK;
+            if constexpr (mf) {
+                if constexpr (!(HAS_PV && n < PRE)) {
+                    constexpr int lastf = (n + PRE) < NF - 1 ? (n + PRE) : NF - 1;
+                    wait_lgkm<reads_between<NFV, NFK, HAS_PV, HAS_QK, PREF>(n + 1, lastf)>();
+                }
+                if constexpr (s < NS_PV) {
+                    constexpr int ch = n / DT, t = n % DT;
+                    u32x4 a;
+                    if constexpr (n < PRE) a = u32x4{pre_lo[n][0], pre_lo[n][1], pre_hi[n][0], pre_hi[n][1]};
+                    else a = u32x4{vlo[n][0], vlo[n][1], vhi[n][0], vhi[n][1]};
+                    mfma_o(oacc[g][t], a, __builtin_bit_cast(u32x4, pf[g][ch]));
+                } else {
+                    constexpr int q = n - NFV, kt = q / KC, kc = q % KC;
+                    if constexpr (kc == 0) mfma_s_first(sacc[g][kt], kfr[q], qa[g][kc]);
+                    else mfma_s(sacc[g][kt], kfr[q], qa[g][kc]);
+                }
+            }
+            // 4. softmax work of this slot
+            if constexpr (HAS_SM) {
+                if constexpr (s < MX) {
+                    constexpr int k0 = s * 16 / MX, k1 = (s + 1) * 16 / MX;
+#pragma unroll
+                    for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+                        for (int k = k0; k < k1; ++k)
+                            mx[gg] = max3f(mx[gg], sacc[gg][k >> 3][(2 * k) & 15], sacc[gg][k >> 3][(2 * k + 1) & 15]);
+                }
+                if constexpr (s == MX) {
+#pragma unroll
+                    for (int gg = 0; gg < 2; ++gg) {
+                        const float mxc = other_half_max(mx[gg]) * ctj[gg];
+                        const bool move = mxc > m[gg] + kRescaleSlack;
+                        const float m_new = move ? mxc : m[gg];
+                        alpha[gg] = exp2_hw(m[gg] - m_new);
+                        moved[gg] = __builtin_amdgcn_ballot_w64(move) != 0;
+                        m[gg] = m_new;
+                        mu[gg] = m_new == neg_inf() ? 0.f : m_new;
+                        lsum[gg] *= alpha[gg];
+                    }
+                }
+                // keys 0..31: fma (reads S before slot NS_PV overwrites it), exp, sum + pack
+                constexpr int S1 = MX + 1, W1 = NS_PV - MX - 1;
+                // keys 32..63: fma before the second QK chain, exp and sum spread to the end
+                constexpr int S2 = NS_PV, W2 = NS_QK / 2;
+                constexpr int S3 = NS_PV + 1, W3 = NS - NS_PV - 2;
+#pragma unroll
+                for (int e = elem_first<S1, W1>(s); e < elem_first<S1, W1>(s + 1); ++e)
+                    x[e / 16][0][e % 16] = fmaf(sacc[e / 16][0][e % 16], ctj[e / 16], -mu[e / 16]);
+#pragma unroll
+                for (int e = elem_first<S1, W1>(s - 1); e < elem_first<S1, W1>(s); ++e)
+                    x[e / 16][0][e % 16] = exp2_hw(x[e / 16][0][e % 16]);
+#pragma unroll
+                for (int e = elem_first<S1, W1>(s - 2); e < elem_first<S1, W1>(s - 1); ++e) {
+                    const int gg = e / 16, i = e % 16;
+                    rsum[gg][0] += x[gg][0][i];
+                    if (i & 1) {
+                        pf[gg][i >> 3][(i & 7) - 1] = (__bf16)(FP8 ? x[gg][0][i - 1] * psj : x[gg][0][i - 1]);
+                        pf[gg][i >> 3][i & 7] = (__bf16)(FP8 ? x[gg][0][i] * psj : x[gg][0][i]);
+                    }
+                }
+#pragma unroll
+                for (int e = elem_first<S2, W2>(s); e < elem_first<S2, W2>(s + 1); ++e)
+                    x[e / 16][1][e % 16] = fmaf(sacc[e / 16][1][e % 16], ctj[e / 16], -mu[e / 16]);
+#pragma unroll
+                for (int e = elem_first<S3, W3>(s); e < elem_first<S3, W3>(s + 1); ++e)
+                    x[e / 16][1][e % 16] = exp2_hw(x[e / 16][1][e % 16]);
+#pragma unroll
+                for (int e = elem_first<S3, W3>(s - 1); e < elem_first<S3, W3>(s); ++e) {
+                    const int gg = e / 16, i = e % 16;
+                    rsum[gg][1] += x[gg][1][i];
+                    if (i & 1) {
+                        pf[gg][2 + (i >> 3)][(i & 7) - 1] = (__bf16)(FP8 ? x[gg][1][i - 1] * psj : x[gg][1][i - 1]);
+                        pf[gg][2 + (i >> 3)][i & 7] = (__bf16)(FP8 ? x[gg][1][i] * psj : x[gg][1][i]);
+                    }
+                }
+                if constexpr (s == NS - 1) {
+#pragma unroll
+                    for (int gg = 0; gg < 2; ++gg) lsum[gg] += rsum[gg][0] + rsum[gg][1];
+                }
+            }
+            // 5. copies of this step, spread over the block
+            if constexpr (ISSUE) {
+                static_for<N_ISSUE>([&](auto ic) {
+                    constexpr int i = decltype(ic)::value;
+                    if constexpr (2 + i * ((NS - 4) / N_ISSUE) == s) issue_part(j, i);
+                });
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        // reads scheduled past the last slot (next-block prefetch of short blocks)
+        static_for<NF>([&](auto fc) {
+            constexpr int f = decltype(fc)::value;
+            if constexpr (f >= PRE && 2 * (f - PRE) >= NS) read(fc);
+        });
+        if constexpr (PREF) {
+#pragma unroll
+            for (int p = 0; p < PRE; ++p) {
+                pre_lo[p] = nlo[p];
+                pre_hi[p] = nhi[p];
+            }
+        }
+    };
+    using T = std::true_type;
+    using F = std::false_type;
+
+    // O of a group whose reference moved: scale the AGPRs in place (their last
+    // MFMA write is a block away; the trailing nops cover the next MFMA read)
+    auto rescale = [&]() {
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+            if (moved[g]) {
+#pragma unroll
+                for (int t = 0; t < DT; ++t)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        float tmp;
+                        asm volatile("v_accvgpr_read_b32 %1, %0\n\t"
+                                     "v_mul_f32 %1, %1, %2\n\t"
+                                     "v_accvgpr_write_b32 %0, %1"
+                                     : "+a"(oacc[g][t][i]), "=&v"(tmp)
+                                     : "v"(alpha[g]));
+                    }
+                moved[g] = false;
+                asm volatile("s_nop 4");
+            }
+    };
+    // the step before block j: V(j) and K(j+1) in (fp8: V(j) stored), barrier
+    auto mid = [&](int j) {
         if constexpr (FP8) {
-            if (next_v8) {
-                wait_v8(ahead ? L::DMA : 0);
-                store_v8(j + 1);
-            }
+            wait_vm(j == 0 ? 0 : L::K_DMA);
+            store_v8(j);
+            ctj[0] = cg[0] * ks_h[min(j, n_tiles - 1) * kBC / kScaleBlock];
+            ctj[1] = cg[1] * ks_h[min(j, n_tiles - 1) * kBC / kScaleBlock];
+            psj = vs_h[min(j, n_tiles - 1) * kBC / kScaleBlock];
+            asm volatile("" : "+v"(ctj[0]), "+v"(ctj[1]), "+v"(psj));
+        } else {
+            wait_vm(L::V_DMA + L::K_DMA);
         }
-        wait_vm(in_flight);
         lds_barrier();
+    };
+
+    // ---- prologue ----
+    for (int i = tid; i < L::LDS / 16; i += kThreads3) reinterpret_cast<u32x4 *>(smem)[i] = u32x4{};
+    lds_barrier();
+    if constexpr (FP8) {
+#pragma unroll
+        for (int jj = 0; jj < 3; ++jj)
+#pragma unroll
+            for (int i = 0; i < L::K_DMA; ++i) issue_k_part(jj, i);
+#pragma unroll
+        for (int i = 0; i < L::V8_LOADS; ++i) issue_v_part(0, i);
+        wait_vm(2 * L::K_DMA + L::V8_LOADS);     // Q and K(0)
+    } else {
+#pragma unroll
+        for (int i = 0; i < L::K_DMA; ++i) issue_k_part(0, i);
+#pragma unroll
+        for (int i = 0; i < L::V_DMA; ++i) issue_v_part(0, i);
+#pragma unroll
+        for (int i = 0; i < L::K_DMA; ++i) issue_k_part(1, i);
+#pragma unroll
+        for (int i = 0; i < L::V_DMA; ++i) issue_v_part(1, i);
+#pragma unroll
+        for (int i = 0; i < L::K_DMA; ++i) issue_k_part(2, i);
+        wait_vm(2 * L::K_DMA + 2 * L::V_DMA);     // Q and K(0)
     }
-
-
-    // epilogue: O = O~ / l_bf16 ; L = (m + log2 l) ln 2
-    const float lt = other_half_sum(lsum);
-    const float ltb = other_half_sum(lsumb);
-    if (my_q < N) {
-        const float inv = 1.f / ltb;
-        uint16_t *orow = O + ((size_t)bh * N + my_q) * D;
+    // the loads are asm: pin their results after the wait (a copy placed
+    // before it would read registers still being filled), then move to AGPRs
 #pragma unroll
-        for (int t = 0; t < D / 32; ++t)
+    for (int g = 0; g < 2; ++g)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                u32x2 packed;
-                packed[0] = pack_bf16x2(oacc[t][4 * g + 0] * inv, oacc[t][4 * g + 1] * inv);
-                packed[1] = pack_bf16x2(oacc[t][4 * g + 2] * inv, oacc[t][4 * g + 3] * inv);
-                *reinterpret_cast<u32x2 *>(orow + t * 32 + 8 * g + 4 * hf) = packed;
-            }
-        if (LSE && hf == 0) LSE[(size_t)bh * N + my_q] = (m + __log2f(lt)) * kLn2;
+        for (int kc = 0; kc < KC; ++kc) asm volatile("" : "+v"(qa[g][kc]));
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) asm volatile("" : "+a"(qa[g][kc]));
+    asm volatile("s_nop 7");
+    lds_barrier();
+    block(-1, false, F{}, T{}, F{}, F{}, F{});        // S(0) = K(0) Q^T
+
+    // ---- block 0 ----
+    mid(0);
+    if (last >= 1) block(0, 0 >= j_mask, F{}, T{}, T{}, T{}, T{});
+    else block(0, true, F{}, F{}, T{}, T{}, T{});
+    // ---- blocks 1 .. last-1 ----
+    for (int j = 1; j < last; ++j) {
+        rescale();
+        mid(j);
+        block(j, false, T{}, T{}, T{}, T{}, T{});
+    }
+    // ---- block last ----
+    if (last >= 1) {
+        rescale();
+        mid(last);
+        block(last, last >= j_mask, T{}, F{}, T{}, T{}, T{});
+    }
+    // ---- PV(last) with the fragments read ahead by the block before (no
+    // step in between, so wait for those reads here) ----
+    rescale();
+    wait_lgkm<0>();
+    block(last + 1, false, T{}, F{}, F{}, F{}, F{});
+    // causal: the remaining copies are issued for the other waves
+    for (int j = last + 1; j < n_tiles; ++j) {
+        mid(j);
+#pragma unroll
+        for (int i = 0; i < N_ISSUE; ++i) issue_part(j, i);
+    }
+    wait_vm(0);
+    // fp8: the last register loads of V are never stored; keeping them live
+    // up to the wait stops their registers from being reused while in flight
+#pragma unroll
+    for (int i = 0; i < L::V8_LOADS; ++i) asm volatile("" : "+v"(v8reg[i]));
+    asm volatile("s_nop 15\n\ts_nop 15");
+
+    // ---- epilogue: O = O~ / l ; L = (m + log2 l) ln 2 ----
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+        const float lt = other_half_sum(lsum[g]);
+        if (my_q[g] < N) {
+            const float inv = 1.f / lt;
+            uint16_t *orow = O + ((size_t)bh * N + my_q[g]) * D;
+#pragma unroll
+            for (int t = 0; t < DT; ++t)
+#pragma unroll
+                for (int gg = 0; gg < 4; ++gg) {
+                    u32x2 packed;
+                    packed[0] = pack_bf16x2(oacc[g][t][4 * gg + 0] * inv, oacc[g][t][4 * gg + 1] * inv);
+                    packed[1] = pack_bf16x2(oacc[g][t][4 * gg + 2] * inv, oacc[g][t][4 * gg + 3] * inv);
+                    *reinterpret_cast<u32x2 *>(orow + t * 32 + 8 * gg + 4 * hf) = packed;
+                }
+            if (LSE && hf == 0) LSE[(size_t)bh * N + my_q[g]] = (m[g] + __log2f(lt)) * kLn2;
+        }
     }
 }
 
@@ -466,7 +739,7 @@ hipError_t launch_t(const void *q, const void *k, const void *v, const float *qs
     const int n_rb = (N + kBR - 1) / kBR;
     const int BH = B * H;
     const dim3 grid((unsigned)((size_t)BH * n_rb));
-    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, FP8>), grid, dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((fwd_kernel3<D, CAUSAL, FP8>), grid, dim3(kThreads3), 0, stream,
                        static_cast<const uint8_t *>(q), static_cast<const uint8_t *>(k),
                        static_cast<const uint8_t *>(v), qs, ks, vs, static_cast<uint16_t *>(o), lse, N,
                        BH, n_rb, scale * kLog2e);
