@@ -39,9 +39,14 @@ def common_flags():
     ]
 
 
+# per-source flags: the prefill kernel never produces NaN on purpose (masking
+# uses -inf), and without NaN semantics max(max(a, b), c) is one v_max3
+EXTRA = {"fwd_prefill.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + common_flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + common_flags() + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))

@@ -87,9 +87,16 @@ __device__ __forceinline__ u32x4 sgpr_rsrc(const void *base, uint32_t bytes) {
 // which would serialise the prefetch ring.
 
 // 16-byte global -> LDS copy per lane: lane l writes lds_addr + 16 l
+// (an SALU write of M0 needs one wait state before an LDS-DMA reads it)
 __device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                  :: "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
+// the same with the LDS address given as an SGPR base plus a constant
+template <uint32_t IMM>
+__device__ __forceinline__ void dma16c(u32x4 rsrc, uint32_t lds_base, uint32_t voff, uint32_t soff) {
+    asm volatile("s_add_u32 m0, %0, %4\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(lds_base), "v"(voff), "s"(rsrc), "s"(soff), "n"(IMM) : "memory");
 }
 // 16- and 8-byte global -> register loads whose completion is also tracked by hand
 __device__ __forceinline__ u32x4 vload16(u32x4 rsrc, uint32_t voff, uint32_t soff) {
@@ -152,8 +159,7 @@ __device__ __forceinline__ void lds_barrier() {
 // the first fragments of the next block. fp8 V is staged through registers
 // (loaded in block j-1, converted to bf16 and stored before block j).
 constexpr int kThreads3 = 256;
-constexpr int kKRing = 3;
-constexpr int kVRing = 4;
+constexpr int kRing = 4;    // LDS stages of K and of V
 
 template <typename F, int... I>
 __device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
@@ -226,11 +232,8 @@ constexpr int elem_first(int s) {
     while (e < 32 && elem_slot<S0, W>(e) < s) ++e;
     return e;
 }
-__device__ __forceinline__ float max3f(float a, float b, float c) {
-    float r;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
-}
+// (this file is built with -fno-honor-nans, so the two maxes become one v_max3)
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
 
 template <int D, bool FP8>
 struct Layout3 {
@@ -241,7 +244,7 @@ struct Layout3 {
     static constexpr int K_DMA = K_TILE / 1024 / 4;                 // 1 KiB copies per wave
     static constexpr int V_DMA = FP8 ? 0 : V_TILE / 1024 / 4;
     static constexpr int V8_LOADS = FP8 ? kBC * D / 16 / kThreads3 : 0;
-    static constexpr int LDS = kKRing * K_TILE + kVRing * V_TILE;
+    static constexpr int LDS = kRing * (K_TILE + V_TILE);
     static constexpr int KC = D / 16;        // QK k-steps
     static constexpr int DT = D / 32;        // PV output tiles
     static constexpr int NFV = 4 * DT;       // PV fragments (f = ch * DT + t)
@@ -334,10 +337,13 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
         vdma_off[i] = (uint32_t)(r * L::VROW + ((pc ^ swz<VCPR>(r)) << 4));
     }
     const uint32_t lds_k = (uint32_t)(size_t)smem;
-    const uint32_t lds_v = lds_k + kKRing * L::K_TILE;
+    const uint32_t lds_v = lds_k + kRing * L::K_TILE;
+    // this wave's share of a K / V tile in LDS (stage 0)
+    const uint32_t wk_base = __builtin_amdgcn_readfirstlane(lds_k + w * L::K_DMA * 1024);
+    const uint32_t wv_base = __builtin_amdgcn_readfirstlane(lds_v + w * L::V_DMA * 1024);
     auto issue_k_part = [&](int j, int i) {
-        const uint32_t dst = lds_k + (uint32_t)(j % kKRing) * L::K_TILE + (w * L::K_DMA + i) * 1024;
-        dma16(rk, dst, kdma_off[i], (uint32_t)(j * kBC) * L::KROW);
+        dma16(rk, wk_base + (uint32_t)(j & (kRing - 1)) * L::K_TILE + i * 1024, kdma_off[i],
+              (uint32_t)(j * kBC) * L::KROW);
     };
     u32x4 v8reg[L::V8_LOADS > 0 ? L::V8_LOADS : 1];
     auto issue_v_part = [&](int j, int i) {
@@ -345,19 +351,33 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
         if constexpr (FP8) {
             v8reg[i] = vload16(rv, (uint32_t)(tid + i * kThreads3) * 16, soff);
         } else {
-            const uint32_t dst = lds_v + (uint32_t)(j & (kVRing - 1)) * L::V_TILE + (w * L::V_DMA + i) * 1024;
-            dma16(rv, dst, vdma_off[i], soff);
+            dma16(rv, wv_base + (uint32_t)(j & (kRing - 1)) * L::V_TILE + i * 1024, vdma_off[i], soff);
         }
     };
     constexpr int NV_ISSUE = FP8 ? L::V8_LOADS : L::V_DMA;
     constexpr int N_ISSUE = NV_ISSUE + L::K_DMA;
-    // the copies of step j: V first (fp8: V(j+1) into registers; bf16: V(j+2)), then K(j+3)
-    auto issue_part = [&](int j, int i) {
-        if (i < NV_ISSUE) issue_v_part(FP8 ? j + 1 : j + 2, i);
-        else issue_k_part(j + 3, i - NV_ISSUE);
+    // the copies of step j: V first (fp8: V(j+1) into registers; bf16: V(j+2)), then K(j+3).
+    // PH >= 0: j & 3 == PH is known here, so the LDS stages are constants.
+    auto issue_part = [&](int j, auto ic, auto phc) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;
+        constexpr int PH = decltype(phc)::value;
+        if constexpr (PH < 0) {
+            if constexpr (i < NV_ISSUE) issue_v_part(FP8 ? j + 1 : j + 2, i);
+            else issue_k_part(j + 3, i - NV_ISSUE);
+        } else if constexpr (i < NV_ISSUE) {
+            const uint32_t soff = (uint32_t)((FP8 ? j + 1 : j + 2) * kBC) * L::KROW;
+            if constexpr (FP8)
+                v8reg[i] = vload16(rv, (uint32_t)(tid + i * kThreads3) * 16, soff);
+            else
+                dma16c<((PH + 2) & (kRing - 1)) * L::V_TILE + i * 1024>(rv, wv_base, vdma_off[i], soff);
+        } else {
+            constexpr int ik = i - NV_ISSUE;
+            dma16c<((PH + 3) & (kRing - 1)) * L::K_TILE + ik * 1024>(rk, wk_base, kdma_off[ik],
+                                                                     (uint32_t)((j + 3) * kBC) * L::KROW);
+        }
     };
-    auto store_v8 = [&](int j) {
-        uint8_t *sv = smem + kKRing * L::K_TILE + (j & (kVRing - 1)) * L::V_TILE;
+    auto store_v8 = [&](int j) __attribute__((always_inline)) {
+        uint8_t *sv = smem + kRing * L::K_TILE + (j & (kRing - 1)) * L::V_TILE;
 #pragma unroll
         for (int i = 0; i < L::V8_LOADS; ++i) {
             asm volatile("" : "+v"(v8reg[i]));
@@ -396,6 +416,13 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
             voff[rd][t] = (uint32_t)(r * L::VROW + ((cidx ^ swz<VCPR>(r)) << 4) + 8 * (tr_j & 1));
         }
 
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) koff[kc] += lds_k;
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd)
+#pragma unroll
+        for (int t = 0; t < DT; ++t) voff[rd][t] += lds_v;
+
     typedef typename std::conditional<FP8, u32x2, u32x4>::type KF;
     f32x16 oacc[2][DT];
     f32x16 sacc[2][2];          // S^T of the newest tile (VGPR)
@@ -414,34 +441,39 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
 
     // One block. HAS_PV: O += V_{j-1}^T P^T; HAS_QK: S = K_{j+1} Q^T;
     // HAS_SM: softmax of tile j; PREF: read the first V_j fragments for the
-    // next PV; ISSUE: the copies of step j.
+    // next PV; ISSUE: the copies of step j. PH = j & 3 when known (the LDS
+    // stages then go into the instructions' offset fields), else -1.
     auto block = [&](int j, bool masked, auto has_pv_c, auto has_qk_c, auto has_sm_c, auto pref_c,
-                     auto issue_c) {
+                     auto issue_c, auto phc) __attribute__((always_inline)) {
         constexpr bool HAS_PV = decltype(has_pv_c)::value;
         constexpr bool HAS_QK = decltype(has_qk_c)::value;
         constexpr bool HAS_SM = decltype(has_sm_c)::value;
         constexpr bool PREF = decltype(pref_c)::value;
         constexpr bool ISSUE = decltype(issue_c)::value;
+        constexpr int PH = decltype(phc)::value;
         constexpr int NF = NFV + NFK + PRE;
+        constexpr int KIMM = PH < 0 ? 0 : ((PH + 1) & (kRing - 1)) * L::K_TILE;
+        constexpr int VIMM = PH < 0 ? 0 : ((PH + kRing - 1) & (kRing - 1)) * L::V_TILE;
+        constexpr int NIMM = PH < 0 ? 0 : (PH & (kRing - 1)) * L::V_TILE;
         uint32_t ka[KC], va[2][DT], vn[2][DT];
         if constexpr (HAS_QK) {
-            const uint32_t kb = __builtin_amdgcn_readfirstlane(lds_k + (uint32_t)((j + 1) % kKRing) * L::K_TILE);
+            const uint32_t kb = PH < 0 ? (uint32_t)((j + 1) & (kRing - 1)) * L::K_TILE : 0u;
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc) ka[kc] = kb + koff[kc];
+            for (int kc = 0; kc < KC; ++kc) ka[kc] = PH < 0 ? kb + koff[kc] : koff[kc];
         }
         if constexpr (HAS_PV) {
-            const uint32_t vb = __builtin_amdgcn_readfirstlane(lds_v + (uint32_t)((j - 1) & (kVRing - 1)) * L::V_TILE);
+            const uint32_t vb = PH < 0 ? (uint32_t)((j - 1) & (kRing - 1)) * L::V_TILE : 0u;
 #pragma unroll
             for (int rd = 0; rd < 2; ++rd)
 #pragma unroll
-                for (int t = 0; t < DT; ++t) va[rd][t] = vb + voff[rd][t];
+                for (int t = 0; t < DT; ++t) va[rd][t] = PH < 0 ? vb + voff[rd][t] : voff[rd][t];
         }
         if constexpr (PREF) {
-            const uint32_t vb = __builtin_amdgcn_readfirstlane(lds_v + (uint32_t)(j & (kVRing - 1)) * L::V_TILE);
+            const uint32_t vb = PH < 0 ? (uint32_t)(j & (kRing - 1)) * L::V_TILE : 0u;
 #pragma unroll
             for (int rd = 0; rd < 2; ++rd)
 #pragma unroll
-                for (int t = 0; t < DT; ++t) vn[rd][t] = vb + voff[rd][t];
+                for (int t = 0; t < DT; ++t) vn[rd][t] = PH < 0 ? vb + voff[rd][t] : voff[rd][t];
         }
         u32x2 vlo[NFV], vhi[NFV];
         KF kfr[NFK];
@@ -451,26 +483,27 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
             if constexpr (f < NFV) {
                 if constexpr (HAS_PV && f >= PRE) {
                     constexpr int ch = f / DT, t = f % DT;
-                    vlo[f] = ds_tr16<16 * ch * L::VROW>(va[0][t]);
-                    vhi[f] = ds_tr16<16 * ch * L::VROW>(va[1][t]);
+                    vlo[f] = ds_tr16<VIMM + 16 * ch * L::VROW>(va[0][t]);
+                    vhi[f] = ds_tr16<VIMM + 16 * ch * L::VROW>(va[1][t]);
                 }
             } else if constexpr (f < NFV + NFK) {
                 if constexpr (HAS_QK) {
                     constexpr int q = f - NFV, kt = q / KC, kc = q % KC;
-                    if constexpr (FP8) kfr[q] = ds_b64<kt * 32 * L::KROW>(ka[kc]);
-                    else kfr[q] = ds_b128<kt * 32 * L::KROW>(ka[kc]);
+                    if constexpr (FP8) kfr[q] = ds_b64<KIMM + kt * 32 * L::KROW>(ka[kc]);
+                    else kfr[q] = ds_b128<KIMM + kt * 32 * L::KROW>(ka[kc]);
                 }
             } else {
                 if constexpr (PREF) {
                     constexpr int p = f - NFV - NFK, ch = p / DT, t = p % DT;
-                    nlo[p] = ds_tr16<16 * ch * L::VROW>(vn[0][t]);
-                    nhi[p] = ds_tr16<16 * ch * L::VROW>(vn[1][t]);
+                    nlo[p] = ds_tr16<NIMM + 16 * ch * L::VROW>(vn[0][t]);
+                    nhi[p] = ds_tr16<NIMM + 16 * ch * L::VROW>(vn[1][t]);
                 }
             }
         };
 
         // softmax state of this block
         float mx[2] = {neg_inf(), neg_inf()};
+        float mt[2][11];
         float mu[2] = {0.f, 0.f};
         float x[2][2][16];
         float rsum[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
@@ -498,9 +531,11 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
             constexpr int n = s / 2, g = s % 2;
             constexpr bool mf = s < NS_PV ? HAS_PV : HAS_QK;
             if constexpr (mf) {
-                if constexpr (!(HAS_PV && n < PRE)) {
+                // one wait per two fragments: at the first MFMA of an even
+                // fragment n, wait until fragments n and n + 1 are in
+                if constexpr (s % 4 == 0 && !(HAS_PV && n + 1 < PRE)) {
                     constexpr int lastf = (n + PRE) < NF - 1 ? (n + PRE) : NF - 1;
-                    wait_lgkm<reads_between<NFV, NFK, HAS_PV, HAS_QK, PREF>(n + 1, lastf)>();
+                    wait_lgkm<reads_between<NFV, NFK, HAS_PV, HAS_QK, PREF>(n + 2, lastf)>();
                 }
                 if constexpr (s < NS_PV) {
                     constexpr int ch = n / DT, t = n % DT;
@@ -516,13 +551,35 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
             }
             // 4. softmax work of this slot
             if constexpr (HAS_SM) {
-                if constexpr (s < MX) {
-                    constexpr int k0 = s * 16 / MX, k1 = (s + 1) * 16 / MX;
+                // row max of the 32 scores of a lane as a tree of v_max3:
+                // 11 ops in slots [0, MX-2), 4 in slot MX-2, 2 in slot MX-1
+                if constexpr (s < MX - 2) {
+                    constexpr int a0 = s * 11 / (MX - 2), a1 = (s + 1) * 11 / (MX - 2);
 #pragma unroll
                     for (int gg = 0; gg < 2; ++gg)
 #pragma unroll
-                        for (int k = k0; k < k1; ++k)
-                            mx[gg] = max3f(mx[gg], sacc[gg][k >> 3][(2 * k) & 15], sacc[gg][k >> 3][(2 * k + 1) & 15]);
+                        for (int a = a0; a < a1; ++a) {
+                            const int v = 3 * a;
+                            if (a < 10)
+                                mt[gg][a] = max3f(sacc[gg][v >> 4][v & 15], sacc[gg][(v + 1) >> 4][(v + 1) & 15],
+                                                  sacc[gg][(v + 2) >> 4][(v + 2) & 15]);
+                            else
+                                mt[gg][a] = fmaxf(sacc[gg][1][14], sacc[gg][1][15]);
+                        }
+                }
+                if constexpr (s == MX - 2) {
+#pragma unroll
+                    for (int gg = 0; gg < 2; ++gg) {
+                        mt[gg][0] = max3f(mt[gg][0], mt[gg][1], mt[gg][2]);
+                        mt[gg][3] = max3f(mt[gg][3], mt[gg][4], mt[gg][5]);
+                        mt[gg][6] = max3f(mt[gg][6], mt[gg][7], mt[gg][8]);
+                        mt[gg][9] = fmaxf(mt[gg][9], mt[gg][10]);
+                    }
+                }
+                if constexpr (s == MX - 1) {
+#pragma unroll
+                    for (int gg = 0; gg < 2; ++gg)
+                        mx[gg] = fmaxf(max3f(mt[gg][0], mt[gg][3], mt[gg][6]), mt[gg][9]);
                 }
                 if constexpr (s == MX) {
 #pragma unroll
@@ -581,7 +638,7 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
             if constexpr (ISSUE) {
                 static_for<N_ISSUE>([&](auto ic) {
                     constexpr int i = decltype(ic)::value;
-                    if constexpr (2 + i * ((NS - 4) / N_ISSUE) == s) issue_part(j, i);
+                    if constexpr (2 + i * ((NS - 4) / N_ISSUE) == s) issue_part(j, ic, phc);
                 });
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -598,13 +655,22 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
                 pre_hi[p] = nhi[p];
             }
         }
+        // fix the block's softmax results here, so that none of its work is
+        // sunk into the next block
+        if constexpr (HAS_SM) {
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                asm volatile("" : "+v"(pf[g][0]), "+v"(pf[g][1]), "+v"(pf[g][2]), "+v"(pf[g][3]));
+                asm volatile("" : "+v"(lsum[g]), "+v"(m[g]), "+v"(alpha[g]));
+            }
+        }
     };
     using T = std::true_type;
     using F = std::false_type;
 
     // O of a group whose reference moved: scale the AGPRs in place (their last
     // MFMA write is a block away; the trailing nops cover the next MFMA read)
-    auto rescale = [&]() {
+    auto rescale = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int g = 0; g < 2; ++g)
             if (moved[g]) {
@@ -624,7 +690,7 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
             }
     };
     // the step before block j: V(j) and K(j+1) in (fp8: V(j) stored), barrier
-    auto mid = [&](int j) {
+    auto mid = [&](int j) __attribute__((always_inline)) {
         if constexpr (FP8) {
             wait_vm(j == 0 ? 0 : L::K_DMA);
             store_v8(j);
@@ -674,34 +740,42 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
         for (int kc = 0; kc < KC; ++kc) asm volatile("" : "+a"(qa[g][kc]));
     asm volatile("s_nop 7");
     lds_barrier();
-    block(-1, false, F{}, T{}, F{}, F{}, F{});        // S(0) = K(0) Q^T
+    using G = std::integral_constant<int, -1>;   // LDS stages from j at run time
+    block(-1, false, F{}, T{}, F{}, F{}, F{}, G{});        // S(0) = K(0) Q^T
 
     // ---- block 0 ----
     mid(0);
-    if (last >= 1) block(0, 0 >= j_mask, F{}, T{}, T{}, T{}, T{});
-    else block(0, true, F{}, F{}, T{}, T{}, T{});
+    if (last >= 1) block(0, 0 >= j_mask, F{}, T{}, T{}, T{}, T{}, G{});
+    else block(0, true, F{}, F{}, T{}, T{}, T{}, G{});
     // ---- blocks 1 .. last-1 ----
-    for (int j = 1; j < last; ++j) {
+    auto step = [&](int j, auto phc) __attribute__((always_inline)) {
         rescale();
         mid(j);
-        block(j, false, T{}, T{}, T{}, T{}, T{});
+        block(j, false, T{}, T{}, T{}, T{}, T{}, phc);
+    };
+    int j = 1;
+    for (; j + 3 < last; j += 4) {   // unrolled over the 4 LDS stages (j & 3 == 1, 2, 3, 0)
+        step(j, std::integral_constant<int, 1>{});
+        step(j + 1, std::integral_constant<int, 2>{});
+        step(j + 2, std::integral_constant<int, 3>{});
+        step(j + 3, std::integral_constant<int, 0>{});
     }
+    for (; j < last; ++j) step(j, G{});
     // ---- block last ----
     if (last >= 1) {
         rescale();
         mid(last);
-        block(last, last >= j_mask, T{}, F{}, T{}, T{}, T{});
+        block(last, last >= j_mask, T{}, F{}, T{}, T{}, T{}, G{});
     }
     // ---- PV(last) with the fragments read ahead by the block before (no
     // step in between, so wait for those reads here) ----
     rescale();
     wait_lgkm<0>();
-    block(last + 1, false, T{}, F{}, F{}, F{}, F{});
+    block(last + 1, false, T{}, F{}, F{}, F{}, F{}, G{});
     // causal: the remaining copies are issued for the other waves
-    for (int j = last + 1; j < n_tiles; ++j) {
-        mid(j);
-#pragma unroll
-        for (int i = 0; i < N_ISSUE; ++i) issue_part(j, i);
+    for (int jj = last + 1; jj < n_tiles; ++jj) {
+        mid(jj);
+        static_for<N_ISSUE>([&](auto ic) { issue_part(jj, ic, G{}); });
     }
     wait_vm(0);
     // fp8: the last register loads of V are never stored; keeping them live
