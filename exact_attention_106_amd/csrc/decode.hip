@@ -6,7 +6,7 @@
 // sequence s is slot t % 16 of physical page block_table[s][t / 16]; pages
 // may be shared between sequences and are only read here.
 //
-// Kernel 1 (split): one workgroup per (KV chunk of 32 pages, head, sequence).
+// The split kernel: one workgroup per (KV chunk of 32 pages, head, sequence).
 // Each of its 4 waves walks every 4th page of the chunk. A (page, head) block
 // of K or V is 16 tokens x 128 channels of bf16 = 4 KiB contiguous; a wave
 // reads it with four fully coalesced 1 KiB loads, so lane l holds tokens
@@ -18,10 +18,13 @@
 // ("FlashAttention系列优化", FlashAttentionV2 equations), and the chunk's
 // partial (m, l, O~) goes to the workspace. This kernel is HBM-bound: the only
 // traffic that matters is reading each needed page once.
+// Within a full chunk each wave keeps the next page's loads in flight while
+// it consumes one.
 //
-// Kernel 2 (merge): one workgroup per (head, sequence) combines its chunks'
+// The merge kernel: one workgroup per (head, sequence) combines its chunks'
 // partials the same way and writes O (bf16) and L = (m + log2 l) ln 2.
-// Slots past the context in the last page are neither used nor loaded.
+// Slots past the context in the last page may be loaded (they lie in the
+// page) but never contribute.
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -62,10 +65,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     const int p_begin = split * kPPS;
     if (p_begin >= n_pages) return;   // whole workgroup: chunk past the context
     const int p_end = min(n_pages, p_begin + kPPS);
-
     const int tid = threadIdx.x;
+
     const int lane = tid & 63;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int tg = lane >> 4;        // token group: tokens 4i + tg
     const int d0 = 8 * (lane & 15);  // channels d0 .. d0+7
 
@@ -87,37 +90,58 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     for (int e = 0; e < 8; ++e) st.o[e] = 0.f;
 
     const int32_t *bt = block_table + (size_t)s * max_blocks;
-    for (int pg = p_begin + w; pg < p_end; pg += kWaves) {
+    // K and V of one page for this lane: tokens 4i + tg, channels d0 .. d0+7
+    struct Page {
+        u32x4 k[4], v[4];
+    };
+    auto load_page = [&](int pg, Page &pp) {
         const int phys = __builtin_amdgcn_readfirstlane(bt[pg]);
         const size_t base = ((size_t)phys * H + h) * (kPS * kD);
-        const uint16_t *kp = kc + base;
-        const uint16_t *vp = vc + base;
         const int tok0 = pg * kPS;
-        u32x4 kx[4], vx[4];
-        bool valid[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int tok = 4 * i + tg;
-            valid[i] = tok0 + tok < ctx;
-            kx[i] = valid[i] ? *reinterpret_cast<const u32x4 *>(kp + tok * kD + d0) : u32x4{};
-            vx[i] = valid[i] ? *reinterpret_cast<const u32x4 *>(vp + tok * kD + d0) : u32x4{};
+            const bool valid = tok0 + tok < ctx;
+            pp.k[i] = valid ? *reinterpret_cast<const u32x4 *>(kc + base + tok * kD + d0) : u32x4{};
+            pp.v[i] = valid ? *reinterpret_cast<const u32x4 *>(vc + base + tok * kD + d0) : u32x4{};
         }
+    };
+    auto load_full = [&](int phys, Page &pp) {
+        const size_t base = ((size_t)phys * H + h) * (kPS * kD);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int tok = 4 * i + tg;
+            pp.k[i] = *reinterpret_cast<const u32x4 *>(kc + base + tok * kD + d0);
+            pp.v[i] = *reinterpret_cast<const u32x4 *>(vc + base + tok * kD + d0);
+        }
+    };
+    // sum over the 16 lanes of a DPP row (the lanes holding one token)
+    auto row_sum = [](float a) {
+        a += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, a), 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+        a += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, a), 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+        a += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, a), 0x141, 0xF, 0xF, false)); // row_half_mirror
+        a += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, a), 0x140, 0xF, 0xF, false)); // row_mirror
+        return a;
+    };
+    auto consume = [&](int pg, const Page &pp) {
+        const int tok0 = pg * kPS;
         float sc[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             float a = 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                a = fmaf(qv[2 * e], bf16_lo(kx[i][e]), a);
-                a = fmaf(qv[2 * e + 1], bf16_hi(kx[i][e]), a);
+                a = fmaf(qv[2 * e], bf16_lo(pp.k[i][e]), a);
+                a = fmaf(qv[2 * e + 1], bf16_hi(pp.k[i][e]), a);
             }
-            // sum over the 16 lanes that share this token
-            a += __shfl_xor(a, 1);
-            a += __shfl_xor(a, 2);
-            a += __shfl_xor(a, 4);
-            a += __shfl_xor(a, 8);
-            sc[i] = valid[i] ? a : neg_inf();
+            a = row_sum(a);
+            sc[i] = tok0 + 4 * i + tg < ctx ? a : neg_inf();
         }
+        // slots past the context may hold anything (even NaN): their weight
+        // is 0 and their V must not reach the sum
+        u32x4 vv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vv[i] = tok0 + 4 * i + tg < ctx ? pp.v[i] : u32x4{};
         const float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
         const float m_new = fmaxf(st.m, mx);
         const float mu = m_new == neg_inf() ? 0.f : m_new;
@@ -131,13 +155,38 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
             float lo = st.o[2 * e] * alpha, hi = st.o[2 * e + 1] * alpha;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                lo = fmaf(p[i], bf16_lo(vx[i][e]), lo);
-                hi = fmaf(p[i], bf16_hi(vx[i][e]), hi);
+                lo = fmaf(p[i], bf16_lo(vv[i][e]), lo);
+                hi = fmaf(p[i], bf16_hi(vv[i][e]), hi);
             }
             st.o[2 * e] = lo;
             st.o[2 * e + 1] = hi;
         }
         st.m = m_new;
+    };
+    if (p_end - p_begin == kPPS) {
+        // full chunk: this wave's 8 pages are known, so all loads are
+        // unconditional and the next page is always in flight while the
+        // current one is consumed (slots past the context are read but
+        // zeroed in consume)
+        constexpr int NP = kPPS / kWaves;
+        const int pg0 = p_begin + w;
+        // the block-table entries first (scalar loads, off the vector-load queue)
+        int phys[NP];
+#pragma unroll
+        for (int k = 0; k < NP; ++k) phys[k] = bt[pg0 + k * kWaves];
+        Page buf[2];
+        load_full(phys[0], buf[0]);
+#pragma unroll
+        for (int k = 0; k < NP; ++k) {
+            if (k + 1 < NP) load_full(phys[k + 1], buf[(k + 1) & 1]);
+            consume(pg0 + k * kWaves, buf[k & 1]);
+        }
+    } else {
+        for (int pg = p_begin + w; pg < p_end; pg += kWaves) {
+            Page pp;
+            load_page(pg, pp);
+            consume(pg, pp);
+        }
     }
 
     // combine the 4 token groups of the wave (lanes l, l^16, l^32, l^48 share channels)
@@ -183,7 +232,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     }
 }
 
-__global__ __launch_bounds__(kD) void decode_merge_kernel(
+// Merge: one workgroup per (head, sequence). The chunks' partials are copied
+// to LDS with coalesced loads (a batch of up to kMergeBatch chunks at a time,
+// all loads of a batch issued together), then thread t < 128 folds channel t
+// over the batch into its running (m, l, O~) with the rescale identity.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeBatch = 64;
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
     const float *__restrict__ ws, const int32_t *__restrict__ ctx_lens, uint16_t *__restrict__ o,
     float *__restrict__ lse, int H, int max_splits)
 {
@@ -194,19 +249,32 @@ __global__ __launch_bounds__(kD) void decode_merge_kernel(
     const int n_pages = (ctx + kPS - 1) / kPS;
     const int n_splits = (n_pages + kPPS - 1) / kPPS;
     const float *src = ws + ((size_t)s * H + h) * max_splits * kPF;
-
-    float mm = neg_inf();
-    for (int k = 0; k < n_splits; ++k) mm = fmaxf(mm, src[k * kPF]);
-    const float mu = mm == neg_inf() ? 0.f : mm;
-    float l = 0.f, acc = 0.f;
-    for (int k = 0; k < n_splits; ++k) {
-        const float wk = exp2_hw(src[k * kPF] - mu);
-        l += wk * src[k * kPF + 1];
-        acc += wk * src[k * kPF + 2 + tid];
+    __shared__ float part[kMergeBatch * kPF];
+    float m = neg_inf(), l = 0.f, acc = 0.f;
+    for (int b0 = 0; b0 < n_splits; b0 += kMergeBatch) {
+        const int nb = min(kMergeBatch, n_splits - b0);
+        __syncthreads();
+        for (int i = tid; i < nb * kPF; i += kMergeThreads) part[i] = src[(size_t)b0 * kPF + i];
+        __syncthreads();
+        if (tid < kD) {
+            float mm = m;
+            for (int k = 0; k < nb; ++k) mm = fmaxf(mm, part[k * kPF]);
+            const float mu = mm == neg_inf() ? 0.f : mm;
+            const float a = exp2_hw(m - mu);
+            l *= a;
+            acc *= a;
+            for (int k = 0; k < nb; ++k) {
+                const float wk = exp2_hw(part[k * kPF] - mu);
+                l += wk * part[k * kPF + 1];
+                acc += wk * part[k * kPF + 2 + tid];
+            }
+            m = mm;
+        }
     }
+    if (tid >= kD) return;
     const float out = l > 0.f ? acc / l : 0.f;
     o[((size_t)s * H + h) * kD + tid] = __builtin_bit_cast(uint16_t, (__bf16)out);
-    if (lse && tid == 0) lse[(size_t)s * H + h] = l > 0.f ? (mm + __log2f(l)) * kLn2 : neg_inf();
+    if (lse && tid == 0) lse[(size_t)s * H + h] = l > 0.f ? (m + __log2f(l)) * kLn2 : neg_inf();
 }
 
 }  // namespace
@@ -228,7 +296,7 @@ hipError_t launch_paged_decode(const void *q, const void *kcache, const void *vc
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 g2((unsigned)H, (unsigned)num_seqs);
-    hipLaunchKernelGGL(decode_merge_kernel, g2, dim3(kD), 0, stream, workspace, ctx_lens,
+    hipLaunchKernelGGL(decode_merge_kernel, g2, dim3(kMergeThreads), 0, stream, workspace, ctx_lens,
                        static_cast<uint16_t *>(o), lse, H, max_splits);
     return hipGetLastError();
 }
