@@ -65,8 +65,7 @@ size_t fa_paged_decode_workspace_bytes(int num_seqs, int H, int d, int page_size
 {
     if (num_seqs <= 0 || H <= 0 || max_blocks_per_seq <= 0) return 0;
     if (d != 128 || page_size != 16) return 0;
-    return (size_t)num_seqs * H * fa::decode_max_splits(max_blocks_per_seq) *
-           fa::decode_partial_floats(d) * sizeof(float);
+    return fa::decode_workspace_bytes(num_seqs, H, max_blocks_per_seq);
 }
 
 fa_status fa_paged_decode(const void *q, const void *kcache, const void *vcache,

@@ -52,42 +52,112 @@ __device__ __forceinline__ void merge_into(State &a, float m2, float l2, const f
     a.m = mm;
 }
 
-__global__ __launch_bounds__(256) void decode_split_kernel(
+// ---- prefix sharing between sequences (PagedAttention section) ----
+// Two sequences whose block tables name the same 32 pages for a full chunk
+// read those pages once: the lower-ranked of a pair computes both queries'
+// partials. Pairs are formed in sequence order inside each class of equal
+// chunks (members m0 < m1 < m2 ...: (m0, m1), (m2, m3), ...).
+// pair[s][c] = partner index, -1 alone, -2 handled by the partner.
+// every slot of chunk c lies inside sequence s's context
+__device__ __forceinline__ bool chunk_full(const int32_t *ctx_lens, int s, int c) {
+    return (c + 1) * kPPS * kPS <= ctx_lens[s];
+}
+__global__ __launch_bounds__(256) void decode_hash_kernel(const int32_t *__restrict__ block_table,
+                                                          const int32_t *__restrict__ ctx_lens,
+                                                          uint64_t *__restrict__ hash, int *__restrict__ n_pairs,
+                                                          int S, int max_blocks, int max_splits) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i == 0) *n_pairs = 0;   // the pair list of this call starts empty
+    if (i >= S * max_splits) return;
+    const int s = i / max_splits, c = i % max_splits;
+    uint64_t hv = 0;   // 0 marks "not a full chunk"
+    if (chunk_full(ctx_lens, s, c)) {
+        const int32_t *e = block_table + (size_t)s * max_blocks + c * kPPS;
+        hv = 1469598103934665603ull;   // FNV-1a over the 32 entries
+        for (int k = 0; k < kPPS; ++k) {
+            hv ^= (uint32_t)e[k];
+            hv *= 1099511628211ull;
+        }
+        hv |= 1;
+    }
+    hash[i] = hv;
+}
+__global__ __launch_bounds__(256) void decode_pair_kernel(const int32_t *__restrict__ block_table,
+                                                          const uint64_t *__restrict__ hash,
+                                                          int *__restrict__ pair, int *__restrict__ n_pairs,
+                                                          int *__restrict__ pair_list, int S, int max_blocks,
+                                                          int max_splits) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= S * max_splits) return;
+    const int s = i / max_splits, c = i % max_splits;
+    const uint64_t hv = hash[i];
+    int res = -1;
+    if (hv != 0) {
+        const int32_t *e = block_table + (size_t)s * max_blocks + c * kPPS;
+        auto same = [&](int t) {
+            if (hash[(size_t)t * max_splits + c] != hv) return false;
+            const int32_t *f = block_table + (size_t)t * max_blocks + c * kPPS;
+            for (int k = 0; k < kPPS; ++k)
+                if (f[k] != e[k]) return false;
+            return true;
+        };
+        int rank = 0;
+        for (int t = 0; t < s; ++t) rank += same(t);
+        if (rank & 1) {
+            res = -2;
+        } else {
+            for (int t = s + 1; t < S; ++t)
+                if (same(t)) {
+                    res = t;
+                    break;
+                }
+        }
+    }
+    pair[i] = res;
+    if (res >= 0) pair_list[atomicAdd(n_pairs, 1)] = i;   // (s, c) of a pair leader
+}
+
+// One (chunk, head, sequence) with NQ = 1 query, or a shared chunk with the
+// queries of a pair (NQ = 2).
+template <int NQ>
+__device__ __forceinline__ void split_chunk(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc,
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ ctx_lens,
-    float *__restrict__ ws, int H, int max_blocks, int max_splits, float c)
+    float *__restrict__ ws, int H, int max_blocks, int max_splits, float c, int split, int h, int s,
+    int partner)
 {
-    const int split = blockIdx.x;
-    const int h = blockIdx.y;
-    const int s = blockIdx.z;
     const int ctx = ctx_lens[s];
     const int n_pages = (ctx + kPS - 1) / kPS;
     const int p_begin = split * kPPS;
-    if (p_begin >= n_pages) return;   // whole workgroup: chunk past the context
     const int p_end = min(n_pages, p_begin + kPPS);
     const int tid = threadIdx.x;
+    const int seq[2] = {s, NQ == 2 ? partner : s};
 
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int tg = lane >> 4;        // token group: tokens 4i + tg
     const int d0 = 8 * (lane & 15);  // channels d0 .. d0+7
 
-    // query slice, pre-multiplied by scale * log2 e
-    float qv[8];
-    {
-        const u32x4 raw = *reinterpret_cast<const u32x4 *>(q + ((size_t)s * H + h) * kD + d0);
+    // query slices, pre-multiplied by scale * log2 e
+    float qv[NQ][8];
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+        const u32x4 raw = *reinterpret_cast<const u32x4 *>(q + ((size_t)seq[u] * H + h) * kD + d0);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            qv[2 * e] = bf16_lo(raw[e]) * c;
-            qv[2 * e + 1] = bf16_hi(raw[e]) * c;
+            qv[u][2 * e] = bf16_lo(raw[e]) * c;
+            qv[u][2 * e + 1] = bf16_hi(raw[e]) * c;
         }
     }
 
-    State st;
-    st.m = neg_inf();
-    st.l = 0.f;
+    State stq[NQ];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) st.o[e] = 0.f;
+    for (int u = 0; u < NQ; ++u) {
+        stq[u].m = neg_inf();
+        stq[u].l = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) stq[u].o[e] = 0.f;
+    }
 
     const int32_t *bt = block_table + (size_t)s * max_blocks;
     // K and V of one page for this lane: tokens 4i + tg, channels d0 .. d0+7
@@ -125,43 +195,48 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     };
     auto consume = [&](int pg, const Page &pp) {
         const int tok0 = pg * kPS;
-        float sc[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float a = 0.f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                a = fmaf(qv[2 * e], bf16_lo(pp.k[i][e]), a);
-                a = fmaf(qv[2 * e + 1], bf16_hi(pp.k[i][e]), a);
-            }
-            a = row_sum(a);
-            sc[i] = tok0 + 4 * i + tg < ctx ? a : neg_inf();
-        }
         // slots past the context may hold anything (even NaN): their weight
-        // is 0 and their V must not reach the sum
+        // is 0 and their V must not reach the sum (a shared chunk is full
+        // for both queries)
         u32x4 vv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) vv[i] = tok0 + 4 * i + tg < ctx ? pp.v[i] : u32x4{};
-        const float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-        const float m_new = fmaxf(st.m, mx);
-        const float mu = m_new == neg_inf() ? 0.f : m_new;
-        const float alpha = exp2_hw(st.m - mu);
-        float p[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p[i] = exp2_hw(sc[i] - mu);
-        st.l = st.l * alpha + (p[0] + p[1]) + (p[2] + p[3]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            float lo = st.o[2 * e] * alpha, hi = st.o[2 * e + 1] * alpha;
+        for (int u = 0; u < NQ; ++u) {
+            State &st = stq[u];
+            float sc[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                lo = fmaf(p[i], bf16_lo(vv[i][e]), lo);
-                hi = fmaf(p[i], bf16_hi(vv[i][e]), hi);
+                float a = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    a = fmaf(qv[u][2 * e], bf16_lo(pp.k[i][e]), a);
+                    a = fmaf(qv[u][2 * e + 1], bf16_hi(pp.k[i][e]), a);
+                }
+                a = row_sum(a);
+                sc[i] = tok0 + 4 * i + tg < ctx ? a : neg_inf();
             }
-            st.o[2 * e] = lo;
-            st.o[2 * e + 1] = hi;
+            const float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+            const float m_new = fmaxf(st.m, mx);
+            const float mu = m_new == neg_inf() ? 0.f : m_new;
+            const float alpha = exp2_hw(st.m - mu);
+            float p[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) p[i] = exp2_hw(sc[i] - mu);
+            st.l = st.l * alpha + (p[0] + p[1]) + (p[2] + p[3]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float lo = st.o[2 * e] * alpha, hi = st.o[2 * e + 1] * alpha;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    lo = fmaf(p[i], bf16_lo(vv[i][e]), lo);
+                    hi = fmaf(p[i], bf16_hi(vv[i][e]), hi);
+                }
+                st.o[2 * e] = lo;
+                st.o[2 * e + 1] = hi;
+            }
+            st.m = m_new;
         }
-        st.m = m_new;
     };
     if (p_end - p_begin == kPPS) {
         // full chunk: this wave's 8 pages are known, so all loads are
@@ -181,7 +256,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
             if (k + 1 < NP) load_full(phys[k + 1], buf[(k + 1) & 1]);
             consume(pg0 + k * kWaves, buf[k & 1]);
         }
-    } else {
+    } else if constexpr (NQ == 1) {
         for (int pg = p_begin + w; pg < p_end; pg += kWaves) {
             Page pp;
             load_page(pg, pp);
@@ -189,46 +264,85 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
         }
     }
 
-    // combine the 4 token groups of the wave (lanes l, l^16, l^32, l^48 share channels)
-#pragma unroll
-    for (int off = 16; off <= 32; off <<= 1) {
-        const float m2 = __shfl_xor(st.m, off);
-        const float l2 = __shfl_xor(st.l, off);
-        float o2[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o2[e] = __shfl_xor(st.o[e], off);
-        merge_into(st, m2, l2, o2);
-    }
-
-    // combine the 4 waves through LDS
+    // combine the 4 token groups of the wave (lanes l, l^16, l^32, l^48 share
+    // channels), then the 4 waves through LDS; one query at a time
     __shared__ float red[kWaves][kPF];
-    if (lane < 16) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) red[w][2 + d0 + e] = st.o[e];
-        if (lane == 0) {
-            red[w][0] = st.m;
-            red[w][1] = st.l;
+    for (int u = 0; u < NQ; ++u) {
+        State &st = stq[u];
+#pragma unroll
+        for (int off = 16; off <= 32; off <<= 1) {
+            const float m2 = __shfl_xor(st.m, off);
+            const float l2 = __shfl_xor(st.l, off);
+            float o2[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o2[e] = __shfl_xor(st.o[e], off);
+            merge_into(st, m2, l2, o2);
+        }
+        if (u > 0) __syncthreads();
+        if (lane < 16) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) red[w][2 + d0 + e] = st.o[e];
+            if (lane == 0) {
+                red[w][0] = st.m;
+                red[w][1] = st.l;
+            }
+        }
+        __syncthreads();
+        if (tid < kD) {
+            float mm = neg_inf();
+#pragma unroll
+            for (int k = 0; k < kWaves; ++k) mm = fmaxf(mm, red[k][0]);
+            const float mu = mm == neg_inf() ? 0.f : mm;
+            float l = 0.f, o = 0.f;
+#pragma unroll
+            for (int k = 0; k < kWaves; ++k) {
+                const float wk = exp2_hw(red[k][0] - mu);
+                l += wk * red[k][1];
+                o += wk * red[k][2 + tid];
+            }
+            float *dst = ws + (((size_t)seq[u] * H + h) * max_splits + split) * kPF;
+            dst[2 + tid] = o;
+            if (tid == 0) {
+                dst[0] = mm;
+                dst[1] = l;
+            }
         }
     }
-    __syncthreads();
-    if (tid < kD) {
-        float mm = neg_inf();
-#pragma unroll
-        for (int k = 0; k < kWaves; ++k) mm = fmaxf(mm, red[k][0]);
-        const float mu = mm == neg_inf() ? 0.f : mm;
-        float l = 0.f, o = 0.f;
-#pragma unroll
-        for (int k = 0; k < kWaves; ++k) {
-            const float wk = exp2_hw(red[k][0] - mu);
-            l += wk * red[k][1];
-            o += wk * red[k][2 + tid];
-        }
-        float *dst = ws + (((size_t)s * H + h) * max_splits + split) * kPF;
-        dst[2 + tid] = o;
-        if (tid == 0) {
-            dst[0] = mm;
-            dst[1] = l;
-        }
+}
+
+// every (chunk, head, sequence) that no pair handles
+__global__ __launch_bounds__(256) void decode_split_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc,
+    const int32_t *__restrict__ block_table, const int32_t *__restrict__ ctx_lens,
+    float *__restrict__ ws, const int *__restrict__ pair, int H, int max_blocks, int max_splits, float c)
+{
+    const int split = blockIdx.x;
+    const int h = blockIdx.y;
+    const int s = blockIdx.z;
+    const int n_pages = (ctx_lens[s] + kPS - 1) / kPS;
+    if (split * kPPS >= n_pages) return;   // whole workgroup: chunk past the context
+    if (pair[(size_t)s * max_splits + split] != -1) return;   // read by a pair
+    split_chunk<1>(q, kc, vc, block_table, ctx_lens, ws, H, max_blocks, max_splits, c, split, h, s, s);
+}
+
+// the shared chunks: a fixed grid walks the pair list (its length is only
+// known on the device); every workgroup leaves when the list is done
+constexpr int kPairGrid = 512;
+__global__ __launch_bounds__(256) void decode_pair_split_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc,
+    const int32_t *__restrict__ block_table, const int32_t *__restrict__ ctx_lens,
+    float *__restrict__ ws, const int *__restrict__ pair, const int *__restrict__ n_pairs,
+    const int *__restrict__ pair_list, int H, int max_blocks, int max_splits, float c)
+{
+    const int n = *n_pairs * H;
+    for (int item = blockIdx.x; item < n; item += gridDim.x) {
+        const int sc = pair_list[item / H];
+        const int h = item % H;
+        const int s = sc / max_splits, split = sc % max_splits;
+        split_chunk<2>(q, kc, vc, block_table, ctx_lens, ws, H, max_blocks, max_splits, c, split, h, s,
+                       pair[sc]);
+        __syncthreads();   // the LDS of the wave combine is reused by the next item
     }
 }
 
@@ -288,11 +402,28 @@ hipError_t launch_paged_decode(const void *q, const void *kcache, const void *vc
     (void)d;
     (void)page_size;
     const int max_splits = decode_max_splits(max_blocks_per_seq);
+    const int n_chunks = num_seqs * max_splits;
+    uint8_t *tail = reinterpret_cast<uint8_t *>(workspace) +
+                    decode_partials_floats(num_seqs, H, max_blocks_per_seq) * sizeof(float);
+    uint64_t *hash = reinterpret_cast<uint64_t *>(tail);
+    int *pair = reinterpret_cast<int *>(tail + (size_t)n_chunks * sizeof(uint64_t));
+    int *pair_list = pair + n_chunks;
+    int *n_pairs = pair_list + n_chunks;
+    const dim3 gp((unsigned)((n_chunks + 255) / 256));
+    const uint16_t *qq = static_cast<const uint16_t *>(q);
+    const uint16_t *kk = static_cast<const uint16_t *>(kcache);
+    const uint16_t *vv = static_cast<const uint16_t *>(vcache);
+    const float c = scale * kLog2e;
+    hipLaunchKernelGGL(decode_hash_kernel, gp, dim3(256), 0, stream, block_table, ctx_lens, hash, n_pairs,
+                       num_seqs, max_blocks_per_seq, max_splits);
+    hipLaunchKernelGGL(decode_pair_kernel, gp, dim3(256), 0, stream, block_table, hash, pair, n_pairs,
+                       pair_list, num_seqs, max_blocks_per_seq, max_splits);
     const dim3 g1((unsigned)max_splits, (unsigned)H, (unsigned)num_seqs);
-    hipLaunchKernelGGL(decode_split_kernel, g1, dim3(256), 0, stream,
-                       static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(kcache),
-                       static_cast<const uint16_t *>(vcache), block_table, ctx_lens, workspace, H,
-                       max_blocks_per_seq, max_splits, scale * kLog2e);
+    hipLaunchKernelGGL(decode_split_kernel, g1, dim3(256), 0, stream, qq, kk, vv, block_table, ctx_lens,
+                       workspace, pair, H, max_blocks_per_seq, max_splits, c);
+    hipLaunchKernelGGL(decode_pair_split_kernel, dim3(kPairGrid), dim3(256), 0, stream, qq, kk, vv,
+                       block_table, ctx_lens, workspace, pair, n_pairs, pair_list, H, max_blocks_per_seq,
+                       max_splits, c);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 g2((unsigned)H, (unsigned)num_seqs);

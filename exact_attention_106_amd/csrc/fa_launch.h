@@ -28,6 +28,18 @@ inline int decode_max_splits(int max_blocks_per_seq) {
 // Floats per split partial: m, l, then d unscaled output values.
 inline size_t decode_partial_floats(int d) { return (size_t)d + 2; }
 
+// Workspace: the partials of every (sequence, head, chunk), d = 128, then per
+// (sequence, chunk) a 64-bit hash, a partner index and a pair-list slot, then
+// the pair-list length.
+inline size_t decode_partials_floats(int num_seqs, int H, int max_blocks_per_seq) {
+    return (size_t)num_seqs * H * decode_max_splits(max_blocks_per_seq) * decode_partial_floats(128);
+}
+inline size_t decode_workspace_bytes(int num_seqs, int H, int max_blocks_per_seq) {
+    return decode_partials_floats(num_seqs, H, max_blocks_per_seq) * sizeof(float) +
+           (size_t)num_seqs * decode_max_splits(max_blocks_per_seq) * (sizeof(uint64_t) + 2 * sizeof(int)) +
+           sizeof(int);
+}
+
 hipError_t launch_paged_decode(const void *q, const void *kcache, const void *vcache,
                                const int32_t *block_table, const int32_t *ctx_lens, void *o,
                                float *lse, int num_seqs, int H, int d, int page_size,

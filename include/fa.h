@@ -79,8 +79,10 @@ fa_status fa_fwd_fp8(const uint8_t *q8, const uint8_t *k8, const uint8_t *v8,
 
 /*
  * Bytes of device workspace fa_paged_decode needs for these sizes (the split
- * partials (m, l, unscaled O) of every (sequence, head, KV chunk)). Returns 0
- * for unsupported sizes.
+ * partials (m, l, unscaled O) of every (sequence, head, KV chunk of 32
+ * pages), then per (sequence, chunk) a 64-bit hash and a partner index used
+ * to read chunks shared between sequences once). Returns 0 for unsupported
+ * sizes.
  */
 size_t fa_paged_decode_workspace_bytes(int num_seqs, int H, int d, int page_size,
                                        int max_blocks_per_seq);
@@ -99,7 +101,8 @@ size_t fa_paged_decode_workspace_bytes(int num_seqs, int H, int d, int page_size
  *             the rest are ignored (pad with -1). Pages may be shared.
  *   ctx_lens: int32 [num_seqs], each in [1, max_blocks_per_seq * page_size]
  *             (0 gives O = 0 and L = -inf). Slots past the context in the last
- *             page are never read.
+ *             page may be loaded (they lie inside the page) but never
+ *             contribute, whatever they hold.
  *   o:        bf16 [num_seqs, H, d];  lse: fp32 [num_seqs, H] or NULL.
  *   workspace: device memory of at least fa_paged_decode_workspace_bytes(...)
  *             bytes; contents on entry do not matter.

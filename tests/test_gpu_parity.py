@@ -267,6 +267,42 @@ def test_decode_edge_contexts(fa, gpu):
     assert_close("decode edges", f64_bf16(o), l.cpu().double().numpy(), ro, rl, 2e-2, 1e-3)
 
 
+def test_decode_shared_prefix_classes(fa, gpu):
+    # Sequences 0..5 name the same first 80 pages (two full 32-page chunks and
+    # part of a third), sequence 6 shares 40 pages with 0 and the rest have
+    # their own: a class of six chunk-sharers, read in pairs, plus chunks that
+    # are shared only partly. Contexts differ inside the shared pages' range.
+    p = inputs.paged_pool(num_seqs=9, H=2, d=128, ctx_lo=1300, ctx_hi=2600, seed=61, share=0.0,
+                          nan_tails=False)
+    ctx = torch.tensor([2600, 1300, 1350, 2100, 1290, 2048, 1700, 900, 1024], dtype=torch.int32)
+    p.ctx_lens = ctx
+    nb = (ctx + 15) // 16
+    P = p.kcache.shape[0]
+    bt = torch.full_like(p.block_table, -1)
+    g = torch.Generator().manual_seed(7)
+    own = torch.randperm(P, generator=g).int()
+    nxt = 0
+    def fresh(n):
+        nonlocal nxt
+        r = own[nxt:nxt + n]
+        nxt += n
+        return r
+    bt[0, :nb[0]] = fresh(int(nb[0]))
+    for s in range(1, 9):
+        k = 80 if s < 6 else (40 if s == 6 else 0)
+        k = min(k, int(nb[s]))
+        bt[s, :k] = bt[0, :k]
+        bt[s, k:nb[s]] = fresh(int(nb[s]) - k)
+    assert nxt <= P
+    p.block_table = bt
+    log("fa_paged_decode shared-prefix classes S9 H2")
+    o, l = _decode(fa, p, gpu)
+    torch.cuda.synchronize()
+    ro, rl = oracle.paged_decode(f64_bf16(p.q), bits16(p.kcache), bits16(p.vcache), bt.numpy(),
+                                 ctx.numpy(), p.scale)
+    assert_close("decode shared", f64_bf16(o), l.cpu().double().numpy(), ro, rl, 2e-2, 1e-3)
+
+
 def test_decode_placement_invariance(fa, gpu):
     p = inputs.paged_pool(num_seqs=6, H=4, d=128, ctx_lo=100, ctx_hi=900, seed=51, share=0.5)
     log("fa_paged_decode placement invariance")
