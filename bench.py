@@ -201,6 +201,11 @@ def main():
     wall = time.perf_counter() - t0
     ms = {name: sum(a.elapsed_time(b) for a, b in ev[name]) / args.steps for name, _ in parts}
     log("mean ms per launch: %s" % ms)
+
+    def spread(name):
+        t = sorted(a.elapsed_time(b) for a, b in ev[name])
+        q = lambda f: t[min(len(t) - 1, int(round(f * (len(t) - 1))))]
+        return {"p10": q(0.1), "median": q(0.5), "p90": q(0.9)}
     if args.calib_copy_mib:
         src = torch.ones(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -225,11 +230,12 @@ def main():
                               "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
                               "traffic": measured_traffic("pmc_fwd_prefill_bf16_causal_B1H32N16384d128.md"),
                               "kernel": "fwd_kernel3<128,causal,bf16>", "launch_ms": ms["prefill"],
-                              "flop_per_launch": f}
+                              "launch_ms_spread": spread("prefill"), "flop_per_launch": f}
     if "fp8" in ms:
         f = prefill_flops(2, 16, 8192, 128, True)
         tf = f / (ms["fp8"] * 1e-3) / 1e12
         result["fp8"] = {"value": tf, "unit": "TFLOP/s", "launch_ms": ms["fp8"],
+                         "launch_ms_spread": spread("fp8"),
                          "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP8_TFLOPS,
                                       "unit": "TFLOP/s", "frac": tf / PEAK_FP8_TFLOPS,
                                       "traffic": measured_traffic("pmc_fwd_prefill_fp8_causal_B2H16N8192d128.md"),
@@ -238,12 +244,14 @@ def main():
         ub, lb = decode_bytes(p5)
         gbs = ub / (ms["decode"] * 1e-3) / 1e9
         result["decode"] = {"value": gbs, "unit": "GB/s", "launch_ms": ms["decode"],
+                            "launch_ms_spread": spread("decode"),
                             "bytes_unique": ub, "bytes_logical": lb,
                             "logical_GBps": lb / (ms["decode"] * 1e-3) / 1e9,
                             "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
                                          "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
                                          "traffic": measured_traffic("pmc_paged_decode_S64H32d128.md"),
-                                         "kernel": "decode_split_kernel + decode_merge_kernel"}}
+                                         "kernel": "decode_hash/pair + decode_split + decode_pair_split "
+                                                   "+ decode_merge kernels"}}
     if result["value"] is None and "decode" in result:
         result["value"], result["unit"] = result["decode"]["value"], "GB/s"
     if not args.no_cpu_baseline and "prefill" in only:
