@@ -36,13 +36,15 @@
 // same page done inside one wave.
 //
 // FP8 (FlashAttention-3 block quantisation, "FlashAttention系列优化",
-// FlashAttentionV3 / FP低精度): S^T = K8 Q8^T on v_mfma_f32_32x32x16_fp8_fp8
-// (products of E4M3 values are exact); a 64-key tile lies in one 128-row scale
-// block, so dequantisation is one scalar per tile folded into the softmax
-// multiplier. V is widened E4M3 -> bf16 (exact) on its way into LDS and P.V
-// runs on bf16 MFMA with the tile's V scale folded into P. P is not quantised
-// to E4M3: with V outliers of tens, a 3-bit mantissa on P would exceed this
-// path's accuracy bound.
+// FlashAttentionV3 / FP低精度): S^T = K8 Q8^T on v_mfma_f32_32x32x64_f8f6f4
+// (E4M3 x E4M3, 64 channels per MFMA, products exact), twice the bf16 MFMA
+// rate. A 64-key tile lies in one 128-row scale block, so dequantisation is
+// one scalar per tile: the Q and K scales join the softmax multiplier and
+// log2 of the V scale joins the exponent's bias (P of the tile comes out
+// multiplied by the V scale; l takes its sum back in plain units). V is
+// widened E4M3 -> bf16 (exact) on its way into LDS and P.V runs on bf16 MFMA.
+// P is not quantised to E4M3: with V outliers of tens, a 3-bit mantissa on P
+// would exceed this path's accuracy bound.
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -56,6 +58,8 @@ constexpr int kBC = 64;        // keys per tile
 constexpr int kScaleBlock = 128;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 
 template <int CPR>
 __device__ __forceinline__ int swz(int r) {
@@ -63,10 +67,12 @@ __device__ __forceinline__ int swz(int r) {
     else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
-// two E4M3 bytes (selected 16-bit half of w) -> two bf16 in one dword, exact
+// two E4M3 bytes (selected 16-bit half of w) -> two bf16 in one dword; with
+// a unit scale the conversion is exact (every E4M3 value is a bf16 value)
 __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w, bool hi) {
-    const f32x2 f = hi ? __builtin_amdgcn_cvt_pk_f32_fp8(w, true) : __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-    return (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xffff0000u);
+    const bf16x2 r = hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+                        : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+    return __builtin_bit_cast(uint32_t, r);
 }
 
 // Plain buffer descriptor (base, no stride, num_records = bytes, raw access):
@@ -196,11 +202,12 @@ __device__ __forceinline__ void mfma_s_first(f32x16 &s, u32x4 a, u32x4 b) {
 __device__ __forceinline__ void mfma_s(f32x16 &s, u32x4 a, u32x4 b) {
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "a"(b));
 }
-__device__ __forceinline__ void mfma_s_first(f32x16 &s, u32x2 a, u32x2 b) {
-    asm volatile("v_mfma_f32_32x32x16_fp8_fp8 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "a"(b));
+// E4M3 x E4M3 over 64 channels (both operand formats default to E4M3)
+__device__ __forceinline__ void mfma_s_first(f32x16 &s, u32x8 a, u32x8 b) {
+    asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "a"(b));
 }
-__device__ __forceinline__ void mfma_s(f32x16 &s, u32x2 a, u32x2 b) {
-    asm volatile("v_mfma_f32_32x32x16_fp8_fp8 %0, %1, %2, %0" : "+v"(s) : "v"(a), "a"(b));
+__device__ __forceinline__ void mfma_s(f32x16 &s, u32x8 a, u32x8 b) {
+    asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(s) : "v"(a), "a"(b));
 }
 // O (AGPR) += A (VGPR) x B (VGPR)
 __device__ __forceinline__ void mfma_o(f32x16 &o, u32x4 a, u32x4 b) {
@@ -208,14 +215,14 @@ __device__ __forceinline__ void mfma_o(f32x16 &o, u32x4 a, u32x4 b) {
 }
 
 // LDS reads taken by fragment f of a block (0 if it does not exist)
-template <int NFV, int NFK, bool HAS_PV, bool HAS_QK, bool PREF>
+template <int NFV, int NFK, int KR, bool HAS_PV, bool HAS_QK, bool PREF>
 constexpr int frag_reads(int f) {
-    return f < NFV ? (HAS_PV ? 2 : 0) : f < NFV + NFK ? (HAS_QK ? 1 : 0) : (PREF ? 2 : 0);
+    return f < NFV ? (HAS_PV ? 2 : 0) : f < NFV + NFK ? (HAS_QK ? KR : 0) : (PREF ? 2 : 0);
 }
-template <int NFV, int NFK, bool HAS_PV, bool HAS_QK, bool PREF>
+template <int NFV, int NFK, int KR, bool HAS_PV, bool HAS_QK, bool PREF>
 constexpr int reads_between(int a, int b) {
     int c = 0;
-    for (int f = a; f <= b; ++f) c += frag_reads<NFV, NFK, HAS_PV, HAS_QK, PREF>(f);
+    for (int f = a; f <= b; ++f) c += frag_reads<NFV, NFK, KR, HAS_PV, HAS_QK, PREF>(f);
     return c;
 }
 // fragment f is read in slot 2 (f - PRE); fragments below PRE come from the step before
@@ -245,7 +252,8 @@ struct Layout3 {
     static constexpr int V_DMA = FP8 ? 0 : V_TILE / 1024 / 4;
     static constexpr int V8_LOADS = FP8 ? kBC * D / 16 / kThreads3 : 0;
     static constexpr int LDS = kRing * (K_TILE + V_TILE);
-    static constexpr int KC = D / 16;        // QK k-steps
+    static constexpr int KC = FP8 ? D / 64 : D / 16;   // QK k-steps
+    static constexpr int KR = FP8 ? 2 : 1;   // LDS reads per K fragment
     static constexpr int DT = D / 32;        // PV output tiles
     static constexpr int NFV = 4 * DT;       // PV fragments (f = ch * DT + t)
     static constexpr int NFK = 2 * KC;       // QK fragments (f = kt * KC + kc)
@@ -300,15 +308,17 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
     }
 
     // Q fragments of both groups (B operand of S = K Q^T)
-    typedef typename std::conditional<FP8, u32x2, u32x4>::type QF;
+    typedef typename std::conditional<FP8, u32x8, u32x4>::type QF;
     QF qa[2][KC];
 #pragma unroll
     for (int g = 0; g < 2; ++g)
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
-            if constexpr (FP8)
-                qa[g][kc] = vload8(rq, (uint32_t)(my_q[g] * D + 16 * kc + 8 * hf), 0);
-            else
+            if constexpr (FP8) {
+                const uint32_t a = (uint32_t)(my_q[g] * D + 64 * kc + 32 * hf);
+                qa[g][kc] = __builtin_shufflevector(vload16(rq, a, 0), vload16(rq, a + 16, 0), 0, 1, 2, 3, 4, 5,
+                                                    6, 7);
+            } else
                 qa[g][kc] = vload16(rq, (uint32_t)(my_q[g] * D + 16 * kc + 8 * hf) * 2, 0);
         }
 
@@ -397,14 +407,17 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
     };
 
     // ---- operand-read offsets of this lane ----
-    uint32_t koff[KC];
+    // K fragment of a lane: its key row, channels [64 kc + 32 hf, +32) for
+    // fp8 (two 16-byte chunks), [16 kc + 8 hf, +8) for bf16; Q is loaded with
+    // the same channel assignment, so the pairing in the MFMA is right
+    uint32_t koff[KC][L::KR];
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-        if constexpr (FP8)
-            koff[kc] = (uint32_t)(l32 * L::KROW + ((kc ^ swz<KCPR>(l32)) << 4) + 8 * hf);
-        else
-            koff[kc] = (uint32_t)(l32 * L::KROW + (((2 * kc + hf) ^ swz<KCPR>(l32)) << 4));
-    }
+    for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+        for (int h2 = 0; h2 < L::KR; ++h2) {
+            const int c = FP8 ? 4 * kc + 2 * hf + h2 : 2 * kc + hf;
+            koff[kc][h2] = (uint32_t)(l32 * L::KROW + ((c ^ swz<KCPR>(l32)) << 4));
+        }
     const int tr_G = lane >> 4, tr_e = (lane & 15) >> 2, tr_j = lane & 3;
     uint32_t voff[2][DT];
 #pragma unroll
@@ -417,13 +430,15 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
         }
 
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) koff[kc] += lds_k;
+    for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+        for (int h2 = 0; h2 < L::KR; ++h2) koff[kc][h2] += lds_k;
 #pragma unroll
     for (int rd = 0; rd < 2; ++rd)
 #pragma unroll
         for (int t = 0; t < DT; ++t) voff[rd][t] += lds_v;
 
-    typedef typename std::conditional<FP8, u32x2, u32x4>::type KF;
+    typedef typename std::conditional<FP8, u32x8, u32x4>::type KF;
     f32x16 oacc[2][DT];
     f32x16 sacc[2][2];          // S^T of the newest tile (VGPR)
     bf16x8 pf[2][4];            // P^T of the tile the next PV consumes
@@ -433,7 +448,7 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
     float alpha[2] = {1.f, 1.f};
     bool moved[2] = {false, false};
     float ctj[2] = {cg[0], cg[1]};   // scale (and log2 e) of the current tile
-    float psj = 1.f;                 // V dequant scale of the current tile
+    float lps = 0.f, ipsj = 1.f;     // log2 and inverse of the V dequant scale of the current tile
 #pragma unroll
     for (int g = 0; g < 2; ++g)
 #pragma unroll
@@ -455,11 +470,13 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
         constexpr int KIMM = PH < 0 ? 0 : ((PH + 1) & (kRing - 1)) * L::K_TILE;
         constexpr int VIMM = PH < 0 ? 0 : ((PH + kRing - 1) & (kRing - 1)) * L::V_TILE;
         constexpr int NIMM = PH < 0 ? 0 : (PH & (kRing - 1)) * L::V_TILE;
-        uint32_t ka[KC], va[2][DT], vn[2][DT];
+        uint32_t ka[KC][L::KR], va[2][DT], vn[2][DT];
         if constexpr (HAS_QK) {
             const uint32_t kb = PH < 0 ? (uint32_t)((j + 1) & (kRing - 1)) * L::K_TILE : 0u;
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc) ka[kc] = PH < 0 ? kb + koff[kc] : koff[kc];
+            for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+                for (int h2 = 0; h2 < L::KR; ++h2) ka[kc][h2] = PH < 0 ? kb + koff[kc][h2] : koff[kc][h2];
         }
         if constexpr (HAS_PV) {
             const uint32_t vb = PH < 0 ? (uint32_t)((j - 1) & (kRing - 1)) * L::V_TILE : 0u;
@@ -489,8 +506,11 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
             } else if constexpr (f < NFV + NFK) {
                 if constexpr (HAS_QK) {
                     constexpr int q = f - NFV, kt = q / KC, kc = q % KC;
-                    if constexpr (FP8) kfr[q] = ds_b64<KIMM + kt * 32 * L::KROW>(ka[kc]);
-                    else kfr[q] = ds_b128<KIMM + kt * 32 * L::KROW>(ka[kc]);
+                    if constexpr (FP8)
+                        kfr[q] = __builtin_shufflevector(ds_b128<KIMM + kt * 32 * L::KROW>(ka[kc][0]),
+                                                         ds_b128<KIMM + kt * 32 * L::KROW>(ka[kc][1]), 0, 1, 2,
+                                                         3, 4, 5, 6, 7);
+                    else kfr[q] = ds_b128<KIMM + kt * 32 * L::KROW>(ka[kc][0]);
                 }
             } else {
                 if constexpr (PREF) {
@@ -509,7 +529,11 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
         float rsum[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
         // S was written by the MFMAs at the end of the previous block: cover
         // the MFMA-write -> VALU-access distance before the softmax touches it
-        if constexpr (HAS_SM) asm volatile("s_nop 7\n\ts_nop 7");
+        // (the fp8 QK MFMA has 16 passes, the bf16 one 8)
+        if constexpr (HAS_SM) {
+            if constexpr (FP8) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3");
+            else asm volatile("s_nop 7\n\ts_nop 7");
+        }
         if (HAS_SM && masked) {
             const int k0 = j * kBC;
 #pragma unroll
@@ -535,7 +559,7 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
                 // fragment n, wait until fragments n and n + 1 are in
                 if constexpr (s % 4 == 0 && !(HAS_PV && n + 1 < PRE)) {
                     constexpr int lastf = (n + PRE) < NF - 1 ? (n + PRE) : NF - 1;
-                    wait_lgkm<reads_between<NFV, NFK, HAS_PV, HAS_QK, PREF>(n + 2, lastf)>();
+                    wait_lgkm<reads_between<NFV, NFK, L::KR, HAS_PV, HAS_QK, PREF>(n + 2, lastf)>();
                 }
                 if constexpr (s < NS_PV) {
                     constexpr int ch = n / DT, t = n % DT;
@@ -591,6 +615,7 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
                         moved[gg] = __builtin_amdgcn_ballot_w64(move) != 0;
                         m[gg] = m_new;
                         mu[gg] = m_new == neg_inf() ? 0.f : m_new;
+                        if constexpr (FP8) mu[gg] -= lps;
                         lsum[gg] *= alpha[gg];
                     }
                 }
@@ -610,8 +635,8 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
                     const int gg = e / 16, i = e % 16;
                     rsum[gg][0] += x[gg][0][i];
                     if (i & 1) {
-                        pf[gg][i >> 3][(i & 7) - 1] = (__bf16)(FP8 ? x[gg][0][i - 1] * psj : x[gg][0][i - 1]);
-                        pf[gg][i >> 3][i & 7] = (__bf16)(FP8 ? x[gg][0][i] * psj : x[gg][0][i]);
+                        pf[gg][i >> 3][(i & 7) - 1] = (__bf16)x[gg][0][i - 1];
+                        pf[gg][i >> 3][i & 7] = (__bf16)x[gg][0][i];
                     }
                 }
 #pragma unroll
@@ -625,13 +650,14 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
                     const int gg = e / 16, i = e % 16;
                     rsum[gg][1] += x[gg][1][i];
                     if (i & 1) {
-                        pf[gg][2 + (i >> 3)][(i & 7) - 1] = (__bf16)(FP8 ? x[gg][1][i - 1] * psj : x[gg][1][i - 1]);
-                        pf[gg][2 + (i >> 3)][i & 7] = (__bf16)(FP8 ? x[gg][1][i] * psj : x[gg][1][i]);
+                        pf[gg][2 + (i >> 3)][(i & 7) - 1] = (__bf16)x[gg][1][i - 1];
+                        pf[gg][2 + (i >> 3)][i & 7] = (__bf16)x[gg][1][i];
                     }
                 }
                 if constexpr (s == NS - 1) {
 #pragma unroll
-                    for (int gg = 0; gg < 2; ++gg) lsum[gg] += rsum[gg][0] + rsum[gg][1];
+                    for (int gg = 0; gg < 2; ++gg)
+                        lsum[gg] += FP8 ? (rsum[gg][0] + rsum[gg][1]) * ipsj : rsum[gg][0] + rsum[gg][1];
                 }
             }
             // 5. copies of this step, spread over the block
@@ -696,8 +722,13 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
             store_v8(j);
             ctj[0] = cg[0] * ks_h[min(j, n_tiles - 1) * kBC / kScaleBlock];
             ctj[1] = cg[1] * ks_h[min(j, n_tiles - 1) * kBC / kScaleBlock];
-            psj = vs_h[min(j, n_tiles - 1) * kBC / kScaleBlock];
-            asm volatile("" : "+v"(ctj[0]), "+v"(ctj[1]), "+v"(psj));
+            // P of the tile is computed as vs * exp2(t): log2 vs joins the
+            // exponent's bias and l gets the sum back in units of exp2(t).
+            // Scales below 2^-100 (zero included) act as 2^-100: such a
+            // block's V is 0 to far below bf16 resolution.
+            lps = __builtin_amdgcn_logf(fmaxf(vs_h[min(j, n_tiles - 1) * kBC / kScaleBlock], 0x1p-100f));
+            ipsj = exp2_hw(-lps);
+            asm volatile("" : "+v"(ctj[0]), "+v"(ctj[1]), "+v"(lps), "+v"(ipsj));
         } else {
             wait_vm(L::V_DMA + L::K_DMA);
         }
