@@ -69,8 +69,9 @@ fa_status fa_fwd_f32(const float *q, const float *k, const float *v, float *o, f
  * q8, k8, v8: OCP E4M3FN bytes [B, H, N, d]; q_scale, k_scale, v_scale: fp32
  * [B, H, ceil(N/128)], one per (batch, head, 128-token block); the value of an
  * element is decode(x8) * scale of its block. o: bf16 [B, H, N, d];
- * lse: fp32 [B, H, N] or NULL. d == 128. Q.K^T runs on fp8 MFMA; P.V runs on
- * bf16 MFMA with V widened exactly from E4M3 to bf16.
+ * lse: fp32 [B, H, N] or NULL. d == 128. Scales are finite; v_scale entries
+ * are >= 0, and one below 2^-100 (zero included) acts as 2^-100. Q.K^T runs
+ * on fp8 MFMA; P.V runs on bf16 MFMA with V widened exactly from E4M3 to bf16.
  */
 fa_status fa_fwd_fp8(const uint8_t *q8, const uint8_t *k8, const uint8_t *v8,
                      const float *q_scale, const float *k_scale, const float *v_scale,
