@@ -61,6 +61,8 @@ def _load():
             lib.oracle_dequant_e4m3.restype = None
             lib.oracle_paged_decode.argtypes = [dp, vp, vp, vp, vp, L, I, I, I, L, L, D, dp, dp]
             lib.oracle_paged_decode.restype = I
+            lib.oracle_attention_bwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, L, L, I, D, I]
+            lib.oracle_attention_bwd.restype = I
             _lib = lib
     return _lib
 
@@ -162,3 +164,22 @@ def paged_decode(q, kcache_bits, vcache_bits, block_table, ctx_lens, scale: floa
     if rc != 0:
         raise RuntimeError("oracle_paged_decode failed (%d)" % rc)
     return o, lse
+
+
+def attention_bwd(q, k, v, dout, scale: float, causal: bool):
+    """Gradients (dq, dk, dv) of a loss that reaches attention only through O,
+    given dO: the chain rule through the plain definition (``oracle.c``).
+    q, k, v, dout: [..., n, d]; returns three fp64 arrays of that shape."""
+    q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(dout)
+    shape = q.shape
+    n, d = shape[-2], shape[-1]
+    bh = int(np.prod(shape[:-2])) if len(shape) > 2 else 1
+    for t in (k, v, g):
+        if t.shape != shape:
+            raise ValueError("q, k, v and dout must have the same shape")
+    dq, dk, dv = (np.zeros(shape, dtype=np.float64) for _ in range(3))
+    rc = _load().oracle_attention_bwd(_dptr(q), _dptr(k), _dptr(v), _dptr(g), _dptr(dq),
+                                      _dptr(dk), _dptr(dv), bh, n, d, float(scale), int(bool(causal)))
+    if rc != 0:
+        raise RuntimeError("oracle_attention_bwd failed")
+    return dq, dk, dv

@@ -240,3 +240,88 @@ int oracle_paged_decode(const double *q, const uint16_t *kcache, const uint16_t 
     }
     return err;
 }
+
+/*
+ * Backward pass of the same definition (gradients of a loss that reaches the
+ * attention only through O). The pages describe the backward pass by what it
+ * stores and recomputes, not by formulas (FlashAttention v1 recomputation and
+ * v2 "store only L" on the 91haoming.cn page; the backward part of the
+ * jibinghu.github.io page), so this is the plain chain rule through the three
+ * steps of the forward definition, per head:
+ *   weighted sum o_i = sum_j p_ij v_j :  dv_j  = sum_i p_ij do_i,
+ *                                        dp_ij = do_i . v_j
+ *   softmax p_i = softmax_j(s_ij) over the visible keys (Jacobian
+ *   diag(p) - p p^T):                    ds_ij = p_ij (dp_ij - sum_k p_ik dp_ik)
+ *   similarity s_ij = scale q_i . k_j :  dq_i  = scale sum_j ds_ij k_j,
+ *                                        dk_j  = scale sum_i ds_ij q_i
+ * p is recomputed here from the scores (3-pass safe softmax). A row with no
+ * visible key contributes nothing.
+ * q, k, v, dout [BH, n, d]; dq, dk, dv [BH, n, d] (fp64, contiguous).
+ * Returns 0, or -1 on a bad argument or allocation failure.
+ */
+int oracle_attention_bwd(const double *q, const double *k, const double *v,
+                         const double *dout, double *dq, double *dk, double *dv,
+                         long BH, long n, int d, double scale, int causal)
+{
+    if (!q || !k || !v || !dout || !dq || !dk || !dv || BH < 0 || n < 0 || d <= 0)
+        return -1;
+    int err = 0;
+#pragma omp parallel
+    {
+        double *p = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+        double *dp = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+        if (!p || !dp) {
+#pragma omp atomic write
+            err = -1;
+        } else {
+            /* one head per iteration: dk and dv of a head are sums over its rows */
+#pragma omp for schedule(dynamic, 1)
+            for (long bh = 0; bh < BH; ++bh) {
+                const long off = bh * n * d;
+                const double *qh = q + off, *kh = k + off, *vh = v + off, *gh = dout + off;
+                double *dqh = dq + off, *dkh = dk + off, *dvh = dv + off;
+                for (long x = 0; x < n * d; ++x) dqh[x] = dkh[x] = dvh[x] = 0.0;
+                for (long i = 0; i < n; ++i) {
+                    const long n_vis = causal ? i + 1 : n;
+                    const double *qi = qh + i * d, *gi = gh + i * d;
+                    /* recompute p_i: scores, max, exponentials, sum, normalise */
+                    double m = -INFINITY;
+                    for (long j = 0; j < n_vis; ++j) {
+                        double acc = 0.0;
+                        for (int c = 0; c < d; ++c) acc += qi[c] * kh[j * d + c];
+                        p[j] = scale * acc;
+                        if (p[j] > m) m = p[j];
+                    }
+                    double l = 0.0;
+                    for (long j = 0; j < n_vis; ++j) {
+                        p[j] = exp(p[j] - m);
+                        l += p[j];
+                    }
+                    for (long j = 0; j < n_vis; ++j) p[j] /= l;
+                    /* through the weighted sum */
+                    double pdp = 0.0;
+                    for (long j = 0; j < n_vis; ++j) {
+                        double acc = 0.0;
+                        for (int c = 0; c < d; ++c) {
+                            dvh[j * d + c] += p[j] * gi[c];
+                            acc += gi[c] * vh[j * d + c];
+                        }
+                        dp[j] = acc;
+                        pdp += p[j] * acc;
+                    }
+                    /* through the softmax, then the similarity */
+                    for (long j = 0; j < n_vis; ++j) {
+                        const double ds = p[j] * (dp[j] - pdp);
+                        for (int c = 0; c < d; ++c) {
+                            dqh[i * d + c] += scale * ds * kh[j * d + c];
+                            dkh[j * d + c] += scale * ds * qi[c];
+                        }
+                    }
+                }
+            }
+        }
+        free(p);
+        free(dp);
+    }
+    return err;
+}
