@@ -17,8 +17,9 @@ import torch
 from . import _lib
 from ._lib import FaError
 
-__all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_paged_decode",
-           "fa_paged_decode_workspace_bytes", "fa_status_str", "fa_version", "FaError"]
+__all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_bwd", "fa_bwd_workspace_bytes",
+           "fa_paged_decode", "fa_paged_decode_workspace_bytes", "fa_status_str", "fa_version",
+           "FaError"]
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -126,6 +127,39 @@ def fa_fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, q_scale: to
                                 int(bool(causal)), _stream(q8))
     _lib.check(st, "fa_fwd_fp8")
     return out, lse
+
+
+def fa_bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(_lib.load().fa_bwd_workspace_bytes(B, H, N, d))
+
+
+def fa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+           dout: torch.Tensor, scale: Optional[float] = None, causal: bool = False,
+           workspace: Optional[torch.Tensor] = None, dq: Optional[torch.Tensor] = None,
+           dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None
+           ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """bf16 attention backward for fa_fwd: (dq, dk, dv) bf16 [B, H, N, d] from
+    q/k/v, the forward's O and L (lse), and dO. d in {64, 128}."""
+    B, H, N, d, _ = _dense_common(q, k, v, torch.bfloat16, o, lse, torch.bfloat16)
+    _check_dev("lse", lse, torch.float32, (B, H, N))
+    _check_dev("dout", dout, torch.bfloat16, (B, H, N, d))
+    grads = []
+    for nm, g in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if g is None:
+            g = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q.device)
+        _check_dev(nm, g, torch.bfloat16, (B, H, N, d))
+        grads.append(g)
+    need = fa_bwd_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check_dev("workspace", workspace, (torch.uint8, torch.float32))
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    nbytes = workspace.numel() * workspace.element_size()
+    st = _lib.load().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                            _ptr(grads[0]), _ptr(grads[1]), _ptr(grads[2]), B, H, N, d, scale,
+                            int(bool(causal)), _ptr(workspace), nbytes, _stream(q))
+    _lib.check(st, "fa_bwd")
+    return grads[0], grads[1], grads[2]
 
 
 def fa_paged_decode_workspace_bytes(num_seqs: int, H: int, d: int, page_size: int,

@@ -14,8 +14,8 @@ STATUS_NAMES = {
     4: "FA_ERR_WORKSPACE", 5: "FA_ERR_HIP",
 }
 # every symbol include/fa.h declares
-EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_paged_decode_workspace_bytes",
-           "fa_paged_decode", "fa_status_str", "fa_version")
+EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_bwd_workspace_bytes", "fa_bwd",
+           "fa_paged_decode_workspace_bytes", "fa_paged_decode", "fa_status_str", "fa_version")
 
 
 class FaError(RuntimeError):
@@ -44,6 +44,10 @@ def load() -> ctypes.CDLL:
         lib.fa_fwd_f32.restype = i
         lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
         lib.fa_fwd_fp8.restype = i
+        lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
+        lib.fa_bwd_workspace_bytes.restype = sz
+        lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
+        lib.fa_bwd.restype = i
         lib.fa_paged_decode_workspace_bytes.argtypes = [i, i, i, i, i]
         lib.fa_paged_decode_workspace_bytes.restype = sz
         lib.fa_paged_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]

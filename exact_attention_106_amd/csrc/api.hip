@@ -60,6 +60,27 @@ fa_status fa_fwd_fp8(const uint8_t *q8, const uint8_t *k8, const uint8_t *v8, co
                                        scale, causal, static_cast<hipStream_t>(stream)));
 }
 
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d)
+{
+    if (B <= 0 || H <= 0 || N <= 0 || (d != 64 && d != 128)) return 0;
+    if ((long long)B * H * N * d > kMaxElems) return 0;
+    return fa::bwd_workspace_bytes(B, H, N);
+}
+
+fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                 const void *dout, void *dq, void *dk, void *dv, int B, int H, int N, int d,
+                 float scale, int causal, void *workspace, size_t workspace_bytes, void *stream)
+{
+    fa_status st = check_dense(q, k, v, o, B, H, N, d, scale, causal);
+    if (st != FA_OK) return st;
+    if (!lse || !dout || !dq || !dk || !dv || !workspace) return FA_ERR_NULL_PTR;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (workspace_bytes < fa::bwd_workspace_bytes(B, H, N)) return FA_ERR_WORKSPACE;
+    return from_hip(fa::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal,
+                                        static_cast<float *>(workspace),
+                                        static_cast<hipStream_t>(stream)));
+}
+
 size_t fa_paged_decode_workspace_bytes(int num_seqs, int H, int d, int page_size,
                                        int max_blocks_per_seq)
 {

@@ -57,6 +57,17 @@ __device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t of
     return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
 }
 
+// XOR swizzle of the 16-byte chunks of an LDS row of CPR chunks (CPR = 16:
+// 256-byte rows, CPR = 8: 128-byte rows): chunk c of row r is stored at
+// c ^ swz<CPR>(r). With it, 16-byte reads of one chunk column by 32 rows and
+// the 8-byte transpose reads (ds_read_b64_tr_b16) of 4 x 4 row-chunk blocks
+// are both free of bank conflicts.
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+    if constexpr (CPR == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
 // The running reference max of the online softmax only moves when a row's
 // tile max exceeds it by more than this (base-2 units); until then the terms
 // 2^(t - m) stay below 2^kRescaleSlack, and O~ and l are rescaled only when it

@@ -18,6 +18,14 @@ hipError_t launch_fwd_fp8(const uint8_t *q8, const uint8_t *k8, const uint8_t *v
                           const float *qs, const float *ks, const float *vs, void *o, float *lse,
                           int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
 
+// Backward: fp32 D_i = dO_i . O_i of every row is the only workspace.
+inline size_t bwd_workspace_bytes(int B, int H, int N) { return (size_t)B * H * N * sizeof(float); }
+
+hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const void *o,
+                           const float *lse, const void *dout, void *dq, void *dk, void *dv, int B,
+                           int H, int N, int d, float scale, int causal, float *workspace,
+                           hipStream_t stream);
+
 // Pages per KV chunk (split) of the paged decode.
 constexpr int kDecodePagesPerSplit = 32;
 

@@ -61,11 +61,6 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 
-template <int CPR>
-__device__ __forceinline__ int swz(int r) {
-    if constexpr (CPR == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
-    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-}
 
 // two E4M3 bytes (selected 16-bit half of w) -> two bf16 in one dword; with
 // a unit scale the conversion is exact (every E4M3 value is a bf16 value)

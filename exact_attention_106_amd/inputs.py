@@ -116,6 +116,13 @@ def dense(B: int, H: int, N: int, d: int, seed: int, dtype: str = "bf16",
     return Dense(*tensors, scale=scale, causal=causal, name=name or f"dense_{dtype}_B{B}H{H}N{N}d{d}")
 
 
+def grad_out(B: int, H: int, N: int, d: int, seed: int, device="cpu") -> torch.Tensor:
+    """Seeded upstream gradient dO for the backward pass: standard normal, bf16."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = torch.from_numpy(rng.standard_normal((B, H, N, d), dtype=np.float32))
+    return x.to(torch.bfloat16).to(device)
+
+
 def config2(device="cpu") -> Dense:
     return dense(4, 16, 2048, 64, seed=2, dtype="bf16", scale=1.0 / 8.0, causal=False,
                  device=device, name="mha_bf16_B4H16N2048d64")

@@ -79,6 +79,32 @@ fa_status fa_fwd_fp8(const uint8_t *q8, const uint8_t *k8, const uint8_t *v8,
                      float scale, int causal, void *stream);
 
 /*
+ * Bytes of device workspace fa_bwd needs (fp32 D_i = dO_i . O_i of every row:
+ * B * H * N * 4). Returns 0 for unsupported sizes.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * Attention backward for fa_fwd, bf16 in / bf16 out (fp32 accumulation):
+ * gradients of a loss that reaches the attention through O only.
+ * Recomputation (FlashAttention v1 backward and the v2 "keep only L" change:
+ * 91haoming.cn FlashAttention v1-v3 article; backward part of "Flash
+ * Attention 再学习"): the tiles of P are rebuilt on chip from Q, K and the
+ * logsumexp L of the forward pass; work is parallel over key blocks (each owns
+ * its dK, dV) and, for dQ, over query blocks, without atomics.
+ *   q, k, v, o, dout: bf16 [B, H, N, d] (o: the forward output);
+ *   lse: fp32 [B, H, N], the forward pass's L (natural log);
+ *   dq, dk, dv: bf16 [B, H, N, d], written (not accumulated);
+ *   workspace: device memory of at least fa_bwd_workspace_bytes(B, H, N, d)
+ *   bytes; contents on entry do not matter.
+ * d in {64, 128}; the other sizes, scale and causal are as for fa_fwd.
+ */
+fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                 const void *dout, void *dq, void *dk, void *dv, int B, int H, int N, int d,
+                 float scale, int causal, void *workspace, size_t workspace_bytes,
+                 void *stream);
+
+/*
  * Bytes of device workspace fa_paged_decode needs for these sizes (the split
  * partials (m, l, unscaled O) of every (sequence, head, KV chunk of 32
  * pages), then per (sequence, chunk) a 64-bit hash and a partner index used

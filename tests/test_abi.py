@@ -86,6 +86,26 @@ def test_fp8_validation(lib):
     assert ok
 
 
+def test_bwd_validation(lib):
+    need = lib.fa_bwd_workspace_bytes(2, 4, 1000, 128)
+    assert need == 2 * 4 * 1000 * 4          # fp32 D per row
+    assert lib.fa_bwd_workspace_bytes(2, 4, 1000, 96) == 0
+    assert lib.fa_bwd_workspace_bytes(0, 4, 1000, 128) == 0
+
+    def call(q=FAKE, lse=FAKE, dq=FAKE, ws=FAKE, wsb=need, B=2, N=1000, d=128, scale=0.1, causal=1):
+        return lib.fa_bwd(q, FAKE, FAKE, FAKE, lse, FAKE, dq, FAKE, FAKE, B, 4, N, d, scale, causal,
+                          ws, wsb, None)
+    assert call(q=None) == NULL_PTR
+    assert call(lse=None) == NULL_PTR
+    assert call(dq=None) == NULL_PTR
+    assert call(ws=None) == NULL_PTR
+    assert call(B=0) == BAD_SHAPE
+    assert call(d=96) == UNSUPPORTED
+    assert call(causal=3) == UNSUPPORTED
+    assert call(scale=0.0) == UNSUPPORTED
+    assert call(wsb=need - 1) == WORKSPACE
+
+
 def test_paged_decode_validation(lib):
     need = lib.fa_paged_decode_workspace_bytes(64, 32, 128, 16, 2048)
     # partials (m, l, 128 outputs) per (sequence, head, 32-page chunk), then a

@@ -1,0 +1,113 @@
+"""GPU parity of the attention backward (fa_bwd through the C ABI) against the
+fp64 backward oracle.
+
+Inputs are bf16 (q, k, v, dO); O and L come from fa_fwd on the GPU, as a
+caller would pass them. The oracle differentiates the exact attention of the
+same bf16 inputs. Tolerance per gradient tensor, element by element:
+  |got - ref| <= 1e-2 * max|ref| + half a bf16 ulp of |ref| + 1e-5
+The kernel rounds P and dS to bf16 (relative 2^-9) before they enter the
+MFMA sums, uses the bf16 O for D = dO . O, and rounds the result to bf16 (the
+half-ulp term); against the tensor's largest entry these stay far below 1 %.
+The 1e-5 floor covers fp32 rounding of dP - D, which the mathematics cancels
+exactly in degenerate rows (one visible key: dS = 0) while fp32 sums of 128
+products of unit-size values leave ~1e-7.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_attention_106_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def fa(gpu):
+    import exact_attention_106_amd as fa_mod
+    fa_mod.fa_version()
+    return fa_mod
+
+
+def f64(t):
+    return oracle.bf16_bits_to_f64(t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16))
+
+
+def half_ulp_bf16(x):
+    x = np.abs(x)
+    e = np.floor(np.log2(np.maximum(x, 2.0 ** -126)))
+    return 2.0 ** (e - 8)
+
+
+def check_grad(name, got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    assert np.all(np.isfinite(got)), name + ": non-finite"
+    scale = float(np.max(np.abs(ref))) if ref.size else 0.0
+    err = np.abs(got - ref)
+    tol = 1e-2 * scale + half_ulp_bf16(ref) + 1e-5
+    log("%s: max err %.3e (%.2e of max|ref| %.3e)" % (name, float(err.max()), float(err.max()) / max(scale, 1e-30), scale))
+    assert np.all(err <= tol), "%s: error exceeds tolerance by %.3e" % (name, float(np.max(err - tol)))
+
+
+def run_bwd(fa, gpu, B, H, N, d, causal, seed):
+    x = inputs.dense(B, H, N, d, seed=seed)
+    g = inputs.grad_out(B, H, N, d, seed=seed + 1)
+    q, k, v, do = x.q.to(gpu), x.k.to(gpu), x.v.to(gpu), g.to(gpu)
+    o, lse = fa.fa_fwd(q, k, v, scale=x.scale, causal=causal)
+    dq, dk, dv = fa.fa_bwd(q, k, v, o, lse, do, scale=x.scale, causal=causal)
+    torch.cuda.synchronize()
+    return x, g, (q, k, v, o, lse, do), (dq, dk, dv)
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", [
+    (1, 1, 1, 128, False), (1, 2, 17, 64, False), (1, 2, 17, 64, True),
+    (2, 2, 200, 128, True), (1, 3, 200, 128, False), (2, 1, 513, 64, True),
+    (1, 2, 1000, 128, True), (1, 1, 2049, 128, True), (1, 1, 2049, 64, False)])
+def test_bwd_shapes(fa, gpu, B, H, N, d, causal):
+    log("fa_bwd B%d H%d N%d d%d causal=%d" % (B, H, N, d, causal))
+    x, g, _, grads = run_bwd(fa, gpu, B, H, N, d, causal, seed=500 + N + d + causal)
+    refs = oracle.attention_bwd(f64(x.q), f64(x.k), f64(x.v), f64(g), x.scale, causal)
+    for nm, got, ref in zip(("dq", "dk", "dv"), grads, refs):
+        check_grad("bwd B%dH%dN%dd%d c%d %s" % (B, H, N, d, causal, nm), f64(got), ref)
+
+
+def test_bwd_causal_N4096_d128(fa, gpu):
+    log("fa_bwd causal B1 H1 N4096 d128 (several hundred tiles)")
+    x, g, _, grads = run_bwd(fa, gpu, 1, 1, 4096, 128, True, seed=600)
+    refs = oracle.attention_bwd(f64(x.q), f64(x.k), f64(x.v), f64(g), x.scale, True)
+    for nm, got, ref in zip(("dq", "dk", "dv"), grads, refs):
+        check_grad("bwd N4096 causal " + nm, f64(got), ref)
+
+
+def test_bwd_deterministic_and_causal_future(fa, gpu):
+    # no atomics: two runs agree bit for bit. Causal: changing the last
+    # query's q and dO leaves dq of every earlier row unchanged, bit for bit.
+    log("fa_bwd determinism B1 H2 N700 d128 causal")
+    x, g, ins, grads = run_bwd(fa, gpu, 1, 2, 700, 128, True, seed=700)
+    q, k, v, o, lse, do = ins
+    again = fa.fa_bwd(q, k, v, o, lse, do, scale=x.scale, causal=True)
+    torch.cuda.synchronize()
+    for a, b in zip(grads, again):
+        assert torch.equal(a, b)
+    q2, do2 = q.clone(), do.clone()
+    q2[:, :, -1] += 1.0
+    do2[:, :, -1] -= 1.0
+    o2, lse2 = fa.fa_fwd(q2, k, v, scale=x.scale, causal=True)
+    dq2, _, _ = fa.fa_bwd(q2, k, v, o2, lse2, do2, scale=x.scale, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(grads[0][:, :, :-1], dq2[:, :, :-1])
+
+
+def test_bwd_rejects_bad_arguments(fa, gpu):
+    x = inputs.dense(1, 1, 64, 96, seed=1)
+    t = x.q.to(gpu)
+    o = torch.empty_like(t)
+    lse = torch.empty((1, 1, 64), dtype=torch.float32, device=gpu)
+    with pytest.raises(fa.FaError):
+        fa.fa_bwd(t, t, t, o, lse, t)
