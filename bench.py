@@ -4,6 +4,9 @@ One step = one pass of the whole path over resident synthetic inputs:
   1. fa_fwd      bf16 causal prefill, B=1 H=32 N=16384 d=128   (headline)
   2. fa_fwd_fp8  E4M3 causal prefill, B=2 H=16 N=8192 d=128
   3. fa_paged_decode  64 sequences, H=32, d=128, contexts 512..32768
+  4. fa_bwd      backward of (1) given its O, L and a seeded dO (the first
+                 of the next rows; TFLOP/s on the 5-product count, 2.5x the
+                 forward's)
 Each launch is bracketed by HIP events on the stream it runs on. `value` is
 the prefill's TFLOP/s (4*B*H*N^2*d, halved for causal, per the kernel's mean
 event time); decode GB/s and fp8 TFLOP/s are reported beside it. The CPU
@@ -135,7 +138,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--only", default="", help="comma list of prefill,fp8,decode (default all)")
+    ap.add_argument("--only", default="", help="comma list of prefill,fp8,decode,backward (default all)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -149,7 +152,7 @@ def main():
     import exact_attention_106_amd as fa
     from exact_attention_106_amd import inputs
 
-    only = set(filter(None, args.only.split(","))) or {"prefill", "fp8", "decode"}
+    only = set(filter(None, args.only.split(","))) or {"prefill", "fp8", "decode", "backward"}
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     fa.fa_version()
@@ -177,6 +180,18 @@ def main():
         parts.append(("decode", lambda: fa.fa_paged_decode(p5.q, p5.kcache, p5.vcache, p5.block_table,
                                                            p5.ctx_lens, scale=p5.scale, workspace=ws,
                                                            out=o5, lse=l5)))
+    if "backward" in only:
+        if "prefill" not in only:
+            x3 = inputs.config3()
+            q3, k3, v3 = x3.q.to(dev), x3.k.to(dev), x3.v.to(dev)
+            o3 = torch.empty_like(q3)
+            l3 = torch.empty(q3.shape[:3], dtype=torch.float32, device=dev)
+        fa.fa_fwd(q3, k3, v3, scale=x3.scale, causal=True, out=o3, lse=l3)
+        g3 = inputs.grad_out(1, 32, 16384, 128, seed=6).to(dev)
+        wsb = torch.empty(fa.fa_bwd_workspace_bytes(1, 32, 16384, 128), dtype=torch.uint8, device=dev)
+        dq3, dk3, dv3 = (torch.empty_like(q3) for _ in range(3))
+        parts.append(("backward", lambda: fa.fa_bwd(q3, k3, v3, o3, l3, g3, scale=x3.scale, causal=True,
+                                                    workspace=wsb, dq=dq3, dk=dk3, dv=dv3)))
     torch.cuda.synchronize()
 
     log("warmup %d" % args.warmup)
@@ -252,6 +267,16 @@ def main():
                                          "traffic": measured_traffic("pmc_paged_decode_S64H32d128.md"),
                                          "kernel": "decode_hash/pair + decode_split + decode_pair_split "
                                                    "+ decode_merge kernels"}}
+    if "backward" in ms:
+        f = 2.5 * prefill_flops(1, 32, 16384, 128, True)
+        tf = f / (ms["backward"] * 1e-3) / 1e12
+        result["backward"] = {"value": tf, "unit": "TFLOP/s", "launch_ms": ms["backward"],
+                              "launch_ms_spread": spread("backward"), "flop_per_launch": f,
+                              "workload": "causal bf16 backward B1 H32 N16384 d128",
+                              "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS,
+                                           "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
+                                           "traffic": None,
+                                           "kernel": "bwd_dot + bwd_dkdv + bwd_dq kernels"}}
     if result["value"] is None and "decode" in result:
         result["value"], result["unit"] = result["decode"]["value"], "GB/s"
     if not args.no_cpu_baseline and "prefill" in only:

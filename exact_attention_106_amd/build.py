@@ -41,7 +41,10 @@ def common_flags():
 
 # per-source flags: the prefill kernel never produces NaN on purpose (masking
 # uses -inf), and without NaN semantics max(max(a, b), c) is one v_max3
-EXTRA = {"fwd_prefill.hip": ["-fno-honor-nans"]}
+# backward: MFMA accumulators in VGPRs where they fit (the builtin MFMAs
+# otherwise keep S and dP in AGPRs and copy them out for the softmax)
+EXTRA = {"fwd_prefill.hip": ["-fno-honor-nans"],
+         "bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str) -> str:
