@@ -15,7 +15,8 @@
 // a second kernel parallel over row blocks that recomputes P and dP for its
 // rows: two more tile products per tile instead of atomic adds into an fp32
 // buffer, and the result is deterministic. Three kernels:
-//   bwd_dot:   D_i = dO_i . O_i in fp32 (into the workspace)
+//   bwd_dot:   per row -L_i / scale and -D_i, D_i = dO_i . O_i (fp32, into
+//              the workspace)
 //   bwd_dkdv:  workgroup per (b*h, 128 keys), 4 waves x 32 keys; tiles of 64
 //              queries (Q, dO, L, D) stream through LDS
 //   bwd_dq:    workgroup per (b*h, 128 queries), 4 waves x 32 queries; tiles
@@ -32,6 +33,7 @@
 // only the pairing matters). bwd_dq is the mirror image with queries as
 // columns: S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T.
 #include "fa_device.h"
+#include "fa_dma.h"
 #include "fa_launch.h"
 
 namespace fa {
@@ -77,11 +79,16 @@ __device__ __forceinline__ uint32_t row_offset(int R, int kc, int h) {
 }
 
 // ---------------------------------------------------------------------------
-// D_i = dO_i . O_i, fp32. D / 8 lanes per row, 16 bytes each.
+// Per row: nl_i = -L_i / scale and nd_i = -D_i = -(dO_i . O_i), fp32, into the
+// workspace [2][rows]. They start the S and dP accumulators of bwd_dkdv, so
+// that S - L / scale and dP - D come straight out of the MFMAs. D / 8 lanes
+// per row, 16 bytes each.
 template <int D>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dot_kernel(const uint16_t *__restrict__ O,
                                                               const uint16_t *__restrict__ dO,
-                                                              float *__restrict__ Dlt, long rows)
+                                                              const float *__restrict__ LSE,
+                                                              float *__restrict__ ws, long rows,
+                                                              float inv_scale)
 {
     constexpr int LPR = D / 8;
     const long gid = (long)blockIdx.x * kBwdThreads + threadIdx.x;
@@ -96,21 +103,34 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dot_kernel(const uint16_t *__
     }
 #pragma unroll
     for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
-    if (row < rows && part == 0) Dlt[row] = acc;
+    if (row < rows && part == 0) {
+        ws[row] = -LSE[row] * inv_scale;
+        ws[rows + row] = -acc;
+    }
+}
+
+// S (VGPR, in/out) += A (VGPR) x B (VGPR)
+__device__ __forceinline__ void mfma_acc_v(f32x16 &acc, u32x4 a, u32x4 b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+// O (AGPR, in/out) += A (VGPR) x B (VGPR)
+__device__ __forceinline__ void mfma_acc_a(f32x16 &acc, u32x4 a, u32x4 b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
-    const uint16_t *__restrict__ dO, const float *__restrict__ LSE, const float *__restrict__ Dlt,
+    const uint16_t *__restrict__ dO, const float *__restrict__ NL, const float *__restrict__ ND,
     uint16_t *__restrict__ dK, uint16_t *__restrict__ dV, int N, int BH, float scale)
 {
     constexpr int ROW = 2 * D, CPR = D / 8, KC = D / 16, DT = D / 32;
     constexpr int TILE = kBwdTile * ROW;
-    constexpr int LD = kBwdTile * CPR / kBwdThreads;   // 16-byte loads per thread, tile and tensor
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TILE];   // [stage][Q, dO]
-    __shared__ __attribute__((aligned(16))) float rowv[2][2][kBwdTile]; // [stage][L log2 e, D][query]
+    constexpr int NDMA = TILE / 1024 / 4;              // 1 KiB copies per wave, tile and tensor
+    constexpr int ROWS = 4 * TILE;                      // nl and nd of the two stages after the tiles
+    // [stage][Q, dO] tiles, then [stage][nl, nd][query] fp32
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TILE + 2 * 2 * kBwdTile * 4];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, h = lane >> 5;
     const int kb = blockIdx.x / BH, bh = blockIdx.x % BH;
@@ -119,12 +139,15 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     const int my_key = kw + l32;
     const size_t head = (size_t)bh * N * D;
     const uint32_t head_bytes = (uint32_t)N * ROW;
-    const auto rq = make_rsrc(Q + head, head_bytes);
-    const auto rdo = make_rsrc(dO + head, head_bytes);
     const auto rk = make_rsrc(K + head, head_bytes);
     const auto rv = make_rsrc(V + head, head_bytes);
+    const u32x4 rq = sgpr_rsrc(Q + head, head_bytes);
+    const u32x4 rdo = sgpr_rsrc(dO + head, head_bytes);
+    const u32x4 rnl = sgpr_rsrc(NL + (size_t)bh * N, (uint32_t)N * 4);
+    const u32x4 rnd = sgpr_rsrc(ND + (size_t)bh * N, (uint32_t)N * 4);
 
-    // K and V of this lane's key as B operands (keys past N read zeros)
+    // K and V of this lane's key: B operands (keys past N read zeros); dK^T
+    // and dV^T accumulate in AGPRs
     u32x4 kr[KC], vr[KC];
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
@@ -132,104 +155,167 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
         kr[kc] = buf_load16(rk, off);
         vr[kc] = buf_load16(rv, off);
     }
+    f32x16 dk[DT], dv[DT];
+#pragma unroll
+    for (int t = 0; t < DT; ++t) dk[t] = dv[t] = f32x16{};
+#pragma unroll
+    for (int t = 0; t < DT; ++t) asm volatile("" : "+a"(dk[t]), "+a"(dv[t]));
+
     uint32_t tro[2][DT];
 #pragma unroll
     for (int rd = 0; rd < 2; ++rd)
 #pragma unroll
         for (int t = 0; t < DT; ++t) tro[rd][t] = tr_offset<CPR>(lane, rd, t);
-
-    f32x16 dk[DT], dv[DT];
+    // row-read offsets of this lane (row l32 of a 32-row half; the swizzle
+    // only depends on the row mod 16, so the other half is + 32 ROW)
+    uint32_t rowo[KC];
 #pragma unroll
-    for (int t = 0; t < DT; ++t) dk[t] = dv[t] = f32x16{};
+    for (int kc = 0; kc < KC; ++kc) rowo[kc] = row_offset<CPR>(l32, kc, h);
 
     const int n_qt = (N + kBwdTile - 1) / kBwdTile;
     const int t0 = CAUSAL ? k0 / kBwdTile : 0;
     const float c = scale * kLog2e;
 
-    // tile copies: HBM -> registers (issued before the compute of the
-    // previous tile) -> LDS stage (after it). Rows past N read zeros, and
-    // their L and D are 0: their P is then finite and dO = 0 makes their
+    // Tile copies go from HBM straight into the other LDS stage while the
+    // current tile is computed (each wave copies 1 KiB pieces; the source
+    // chunks are permuted so that the LDS rows come out swizzled). Rows past N
+    // read zeros (nl = nd = 0 too): their P is finite and dO = 0 makes their
     // contributions vanish.
-    u32x4 ldq[LD], lddo[LD];
-    float ldr = 0.f;
-    auto gload = [&](int t) __attribute__((always_inline)) {
+    const uint32_t lds0 = (uint32_t)(size_t)smem;
+    uint32_t dma_off[NDMA];
 #pragma unroll
-        for (int i = 0; i < LD; ++i) {
-            const int idx = tid + i * kBwdThreads;
-            const uint32_t off = (uint32_t)(t * kBwdTile + idx / CPR) * ROW + (idx % CPR) * 16;
-            ldq[i] = buf_load16(rq, off);
-            lddo[i] = buf_load16(rdo, off);
-        }
-        const int q = t * kBwdTile + (tid & 63);
-        ldr = 0.f;
-        if (tid < 128 && q < N) ldr = tid < 64 ? LSE[(size_t)bh * N + q] * kLog2e : Dlt[(size_t)bh * N + q];
-    };
-    auto sstore = [&](int s) __attribute__((always_inline)) {
-        uint8_t *sq = smem + s * 2 * TILE;
+    for (int i = 0; i < NDMA; ++i) {
+        const int pos = (w * NDMA + i) * 64 + lane;
+        const int r = pos / CPR, pc = pos % CPR;
+        dma_off[i] = (uint32_t)(r * ROW + ((pc ^ swz<CPR>(r)) << 4));
+    }
+    auto issue = [&](int t, int st) __attribute__((always_inline)) {
+        const uint32_t soff = (uint32_t)(t * kBwdTile) * ROW;
+        const uint32_t base = __builtin_amdgcn_readfirstlane(lds0 + st * 2 * TILE + w * NDMA * 1024);
 #pragma unroll
-        for (int i = 0; i < LD; ++i) {
-            const int idx = tid + i * kBwdThreads;
-            const int r = idx / CPR, cc = idx % CPR;
-            const uint32_t off = (uint32_t)(r * ROW + ((cc ^ swz<CPR>(r)) << 4));
-            *reinterpret_cast<u32x4 *>(sq + off) = ldq[i];
-            *reinterpret_cast<u32x4 *>(sq + TILE + off) = lddo[i];
+        for (int i = 0; i < NDMA; ++i) {
+            dma16(rq, base + i * 1024, dma_off[i], soff);
+            dma16(rdo, base + TILE + i * 1024, dma_off[i], soff);
         }
-        if (tid < 128) rowv[s][tid >> 6][tid & 63] = ldr;
+        const uint32_t rbase = __builtin_amdgcn_readfirstlane(lds0 + ROWS + (st * 2 + w) * kBwdTile * 4);
+        if (w == 0) dma4(rnl, rbase, (uint32_t)lane * 4, (uint32_t)(t * kBwdTile) * 4);
+        if (w == 1) dma4(rnd, rbase, (uint32_t)lane * 4, (uint32_t)(t * kBwdTile) * 4);
     };
 
-    gload(t0);
-    sstore(0);
-    __syncthreads();
-    for (int t = t0; t < n_qt; ++t) {
-        const int s = (t - t0) & 1;
-        if (t + 1 < n_qt) gload(t + 1);
+    // One tile as a fixed sequence of steps, each with its LDS reads issued
+    // LA steps ahead of its two MFMAs and a share of the elementwise work:
+    //   steps [0, NSD):   S(qt) = Q_qt K^T - L/scale, dP(qt) = dO_qt V^T - D
+    //                     (qt = f / KC; the accumulators start from -L/scale
+    //                     and -D of their queries)
+    //   steps [NSD, NST): dV^T += dO^T P, dK^T += Q^T dS over 16 queries each
+    //   P and dS of qt = 0 are formed during steps [KC, 2 KC), of qt = 1
+    //   during the first 2 DT dV/dK steps (which only use qt = 0).
+    // The MFMAs are inline asm (the compiler cannot see their latency): the
+    // S/dP results are read by VALU only after 20 wait states (s_nop at the
+    // end of steps KC - 1 and NSD - 1), and P/dS written by VALU are read by
+    // an MFMA at least a step later.
+    constexpr int NSD = 2 * KC, NST = NSD + 4 * DT, LA = 4;
+    auto tile = [&](int t, auto sc) __attribute__((always_inline)) {
+        constexpr int S = decltype(sc)::value;
+        constexpr uint32_t QB = S * 2 * TILE, DB = QB + TILE;   // stage bases in LDS
+        const uint8_t *lds = smem;
+        const float *rows = reinterpret_cast<const float *>(smem + ROWS + S * 2 * kBwdTile * 4);
         const int q0 = t * kBwdTile;
-        // causal: a tile whose queries all precede the wave's keys adds nothing
-        if (!CAUSAL || q0 + kBwdTile - 1 >= kw) {
-            const uint8_t *sq = smem + s * 2 * TILE, *sdo = sq + TILE;
-            bf16x8 pb[4], dsb[4];
+        u32x4 ra[NST], rb[NST];
+        f32x16 sacc[2], pacc[2];
+        bf16x8 pb[4], dsb[4];
+        auto read = [&](auto fc) __attribute__((always_inline)) {
+            constexpr int f = decltype(fc)::value;
+            if constexpr (f < NSD) {
+                constexpr int qt = f / KC, kc = f % KC;
+                ra[f] = lds16(lds + QB + qt * 32 * ROW + rowo[kc]);
+                rb[f] = lds16(lds + DB + qt * 32 * ROW + rowo[kc]);
+                if constexpr (kc == 0) {
+                    // element 4a + b of half qt is query qt*32 + 8a + 4h + b
 #pragma unroll
-            for (int qt = 0; qt < 2; ++qt) {
-                f32x16 sacc = {}, pacc = {};
-                const int R = qt * 32 + l32;
+                    for (int a = 0; a < 4; ++a) {
+                        const f32x4 x = *reinterpret_cast<const f32x4 *>(rows + qt * 32 + 8 * a + 4 * h);
+                        const f32x4 y = *reinterpret_cast<const f32x4 *>(rows + kBwdTile + qt * 32 + 8 * a + 4 * h);
 #pragma unroll
-                for (int kc = 0; kc < KC; ++kc) {
-                    const uint32_t off = row_offset<CPR>(R, kc, h);
-                    sacc = mfma(lds16(sq + off), kr[kc], sacc);
-                    pacc = mfma(lds16(sdo + off), vr[kc], pacc);
-                }
-                // element 4a + b of the accumulators is query qt*32 + 8a + 4h + b
-#pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    const f32x4 lv = *reinterpret_cast<const f32x4 *>(&rowv[s][0][qt * 32 + 8 * a + 4 * h]);
-                    const f32x4 dl = *reinterpret_cast<const f32x4 *>(&rowv[s][1][qt * 32 + 8 * a + 4 * h]);
-#pragma unroll
-                    for (int b = 0; b < 4; ++b) {
-                        const int i = 4 * a + b;
-                        float p = exp2_hw(sacc[i] * c - lv[b]);
-                        if (CAUSAL && my_key > q0 + qt * 32 + 8 * a + 4 * h + b) p = 0.f;
-                        const float ds = p * (pacc[i] - dl[b]);
-                        pb[2 * qt + (a >> 1)][4 * (a & 1) + b] = (__bf16)p;
-                        dsb[2 * qt + (a >> 1)][4 * (a & 1) + b] = (__bf16)ds;
+                        for (int b = 0; b < 4; ++b) {
+                            sacc[qt][4 * a + b] = x[b];
+                            pacc[qt][4 * a + b] = y[b];
+                        }
                     }
                 }
+            } else if constexpr (f < NST) {
+                constexpr int kq = (f - NSD) / DT, dt = (f - NSD) % DT;
+                const u32x2 a0 = lds_tr(lds + DB + 16 * kq * ROW + tro[0][dt]);
+                const u32x2 a1 = lds_tr(lds + DB + 16 * kq * ROW + tro[1][dt]);
+                const u32x2 b0 = lds_tr(lds + QB + 16 * kq * ROW + tro[0][dt]);
+                const u32x2 b1 = lds_tr(lds + QB + 16 * kq * ROW + tro[1][dt]);
+                ra[f] = u32x4{a0[0], a0[1], a1[0], a1[1]};
+                rb[f] = u32x4{b0[0], b0[1], b1[0], b1[1]};
             }
-            // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per step
+        };
+        auto elem = [&](int qt, int i) __attribute__((always_inline)) {
+            float p = exp2_hw(sacc[qt][i] * c);
+            if (CAUSAL && my_key > q0 + qt * 32 + 8 * (i >> 2) + 4 * h + (i & 3)) p = 0.f;
+            pb[2 * qt + (i >> 3)][i & 7] = (__bf16)p;
+            dsb[2 * qt + (i >> 3)][i & 7] = (__bf16)(p * pacc[qt][i]);
+        };
+        static_for<LA>([&](auto fc) { read(fc); });
+        static_for<NST>([&](auto fc) {
+            constexpr int f = decltype(fc)::value;
+            read(std::integral_constant<int, f + LA>{});
+            if constexpr (f < NSD) {
+                constexpr int qt = f / KC, kc = f % KC;
+                mfma_acc_v(sacc[qt], ra[f], kr[kc]);
+                mfma_acc_v(pacc[qt], rb[f], vr[kc]);
+                if constexpr (kc == KC - 1) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3");
+            } else {
+                constexpr int kq = (f - NSD) / DT, dt = (f - NSD) % DT;
+                mfma_acc_a(dv[dt], ra[f], __builtin_bit_cast(u32x4, pb[kq]));
+                mfma_acc_a(dk[dt], rb[f], __builtin_bit_cast(u32x4, dsb[kq]));
+            }
+            // elementwise work of half 0 in steps [KC, 2 KC), of half 1 in [NSD, NSD + KC)
+            constexpr int EPS = 16 / KC;
+            if constexpr (f >= KC && f < 2 * KC) {
 #pragma unroll
-            for (int kq = 0; kq < 4; ++kq)
+                for (int i = (f - KC) * EPS; i < (f - KC + 1) * EPS; ++i) elem(0, i);
+            }
+            if constexpr (f >= NSD && f < NSD + KC) {
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    const uint32_t o0 = tro[0][dt] + 16 * kq * ROW, o1 = tro[1][dt] + 16 * kq * ROW;
-                    const u32x2 a0 = lds_tr(sdo + o0), a1 = lds_tr(sdo + o1);
-                    dv[dt] = mfma(u32x4{a0[0], a0[1], a1[0], a1[1]}, __builtin_bit_cast(u32x4, pb[kq]), dv[dt]);
-                    const u32x2 b0 = lds_tr(sq + o0), b1 = lds_tr(sq + o1);
-                    dk[dt] = mfma(u32x4{b0[0], b0[1], b1[0], b1[1]}, __builtin_bit_cast(u32x4, dsb[kq]), dk[dt]);
-                }
-        }
-        if (t + 1 < n_qt) sstore(s ^ 1);
-        __syncthreads();
-    }
+                for (int i = (f - NSD) * EPS; i < (f - NSD + 1) * EPS; ++i) elem(1, i);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        // fix P and dS here so that no elementwise work sinks past the tile
+#pragma unroll
+        for (int k = 0; k < 4; ++k) asm volatile("" : "+v"(pb[k]), "+v"(dsb[k]));
+    };
 
+    // Two tiles per loop iteration, so that the LDS stages are constants and
+    // the accumulators follow one path through the loop (causal tiles whose
+    // queries all precede the wave's keys are computed and masked; a wave
+    // meets at most one).
+    auto step = [&](int t, auto sc) __attribute__((always_inline)) {
+        constexpr int S = decltype(sc)::value;
+        if (t + 1 < n_qt) issue(t + 1, S ^ 1);
+        tile(t, sc);
+        wait_vm_n<0>();
+        __syncthreads();
+    };
+    issue(t0, 0);
+    wait_vm_n<0>();
+    __syncthreads();
+    int t = t0;
+    for (; t + 1 < n_qt; t += 2) {
+        step(t, std::integral_constant<int, 0>{});
+        step(t + 1, std::integral_constant<int, 1>{});
+    }
+    if (t < n_qt) step(t, std::integral_constant<int, 0>{});
+
+    // the last MFMAs wrote dK^T / dV^T: cover the MFMA-write -> read distance
+    // (the pins after the nops keep the reads of the accumulators below them)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3");
+#pragma unroll
+    for (int t = 0; t < DT; ++t) asm volatile("" : "+a"(dk[t]), "+a"(dv[t]));
     // element 4a + b of tile dt is channel 32 dt + 8a + 4h + b of this lane's key
     if (my_key < N) {
         uint16_t *dkp = dK + head + (size_t)my_key * D;
@@ -253,12 +339,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
-    const uint16_t *__restrict__ dO, const float *__restrict__ LSE, const float *__restrict__ Dlt,
+    const uint16_t *__restrict__ dO, const float *__restrict__ NL, const float *__restrict__ ND,
     uint16_t *__restrict__ dQ, int N, int BH, int n_qb, float scale)
 {
     constexpr int ROW = 2 * D, CPR = D / 8, KC = D / 16, DT = D / 32;
     constexpr int TILE = kBwdTile * ROW;
-    constexpr int LD = kBwdTile * CPR / kBwdThreads;
+    constexpr int NDMA = TILE / 1024 / 4;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TILE];   // [stage][K, V]
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, h = lane >> 5;
@@ -270,8 +356,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
     const uint32_t head_bytes = (uint32_t)N * ROW;
     const auto rq = make_rsrc(Q + head, head_bytes);
     const auto rdo = make_rsrc(dO + head, head_bytes);
-    const auto rk = make_rsrc(K + head, head_bytes);
-    const auto rv = make_rsrc(V + head, head_bytes);
+    const u32x4 rk = sgpr_rsrc(K + head, head_bytes);
+    const u32x4 rv = sgpr_rsrc(V + head, head_bytes);
 
     // Q^T and dO^T of this lane's query as B operands; its L and D
     u32x4 qr[KC], dor[KC];
@@ -281,8 +367,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
         qr[kc] = buf_load16(rq, off);
         dor[kc] = buf_load16(rdo, off);
     }
-    const float l2 = my_q < N ? LSE[(size_t)bh * N + my_q] * kLog2e : 0.f;
-    const float dd = my_q < N ? Dlt[(size_t)bh * N + my_q] : 0.f;
+    const float c = scale * kLog2e;
+    // P = 2^(c (S - L / scale)) and dS = P (dP - D) from nl = -L/scale, nd = -D
+    const float nlc = my_q < N ? NL[(size_t)bh * N + my_q] * c : 0.f;
+    const float nd = my_q < N ? ND[(size_t)bh * N + my_q] : 0.f;
     uint32_t tro[2][DT];
 #pragma unroll
     for (int rd = 0; rd < 2; ++rd)
@@ -295,73 +383,113 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
 
     const int kend = CAUSAL ? min(N, qb * kBwdBlock + kBwdBlock) : N;
     const int n_kt = (kend + kBwdTile - 1) / kBwdTile;
-    const float c = scale * kLog2e;
 
-    u32x4 ldk[LD], ldv[LD];
-    auto gload = [&](int t) __attribute__((always_inline)) {
+    // K and V tiles go from HBM straight into the other LDS stage (as in
+    // bwd_dkdv); keys past N read zeros and are masked
+    const uint32_t lds0 = (uint32_t)(size_t)smem;
+    uint32_t dma_off[NDMA];
 #pragma unroll
-        for (int i = 0; i < LD; ++i) {
-            const int idx = tid + i * kBwdThreads;
-            const uint32_t off = (uint32_t)(t * kBwdTile + idx / CPR) * ROW + (idx % CPR) * 16;
-            ldk[i] = buf_load16(rk, off);
-            ldv[i] = buf_load16(rv, off);
-        }
-    };
-    auto sstore = [&](int s) __attribute__((always_inline)) {
-        uint8_t *sk = smem + s * 2 * TILE;
-#pragma unroll
-        for (int i = 0; i < LD; ++i) {
-            const int idx = tid + i * kBwdThreads;
-            const int r = idx / CPR, cc = idx % CPR;
-            const uint32_t off = (uint32_t)(r * ROW + ((cc ^ swz<CPR>(r)) << 4));
-            *reinterpret_cast<u32x4 *>(sk + off) = ldk[i];
-            *reinterpret_cast<u32x4 *>(sk + TILE + off) = ldv[i];
-        }
-    };
-
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int t = 0; t < n_kt; ++t) {
-        const int s = t & 1;
-        if (t + 1 < n_kt) gload(t + 1);
-        const int k0 = t * kBwdTile;
-        // causal: a tile whose keys all follow the wave's queries adds nothing
-        if (!CAUSAL || k0 <= qw + 31) {
-            const uint8_t *sk = smem + s * 2 * TILE, *sv = sk + TILE;
-            bf16x8 dsb[4];
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                f32x16 sacc = {}, pacc = {};
-                const int R = kt * 32 + l32;
-#pragma unroll
-                for (int kc = 0; kc < KC; ++kc) {
-                    const uint32_t off = row_offset<CPR>(R, kc, h);
-                    sacc = mfma(lds16(sk + off), qr[kc], sacc);
-                    pacc = mfma(lds16(sv + off), dor[kc], pacc);
-                }
-                // element 4a + b is key k0 + kt*32 + 8a + 4h + b
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = k0 + kt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-                    float p = exp2_hw(sacc[i] * c - l2);
-                    if (key >= N || (CAUSAL && key > my_q)) p = 0.f;
-                    dsb[2 * kt + (i >> 3)][i & 7] = (__bf16)(p * (pacc[i] - dd));
-                }
-            }
-            // dQ^T += K^T dS^T, 16 keys per step
-#pragma unroll
-            for (int ch = 0; ch < 4; ++ch)
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    const u32x2 a0 = lds_tr(sk + tro[0][dt] + 16 * ch * ROW);
-                    const u32x2 a1 = lds_tr(sk + tro[1][dt] + 16 * ch * ROW);
-                    dq[dt] = mfma(u32x4{a0[0], a0[1], a1[0], a1[1]}, __builtin_bit_cast(u32x4, dsb[ch]), dq[dt]);
-                }
-        }
-        if (t + 1 < n_kt) sstore(s ^ 1);
-        __syncthreads();
+    for (int i = 0; i < NDMA; ++i) {
+        const int pos = (w * NDMA + i) * 64 + lane;
+        const int r = pos / CPR, pc = pos % CPR;
+        dma_off[i] = (uint32_t)(r * ROW + ((pc ^ swz<CPR>(r)) << 4));
     }
+    auto issue = [&](int t, int st) __attribute__((always_inline)) {
+        const uint32_t soff = (uint32_t)(t * kBwdTile) * ROW;
+        const uint32_t base = __builtin_amdgcn_readfirstlane(lds0 + st * 2 * TILE + w * NDMA * 1024);
+#pragma unroll
+        for (int i = 0; i < NDMA; ++i) {
+            dma16(rk, base + i * 1024, dma_off[i], soff);
+            dma16(rv, base + TILE + i * 1024, dma_off[i], soff);
+        }
+    };
+
+    uint32_t rowo[KC];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) rowo[kc] = row_offset<CPR>(l32, kc, h);
+
+    // One tile as a fixed sequence of steps (reads LA steps ahead):
+    //   steps [0, NSD):   S^T(kt) += K_kt Q^T, dP^T(kt) += V_kt dO^T  (kt = f / KC)
+    //   steps [NSD, NST): dQ^T += K^T dS^T over 16 keys each
+    //   dS of kt = 0 is formed during steps [KC, 2 KC), of kt = 1 during the
+    //   first 2 DT dQ steps (which only use kt = 0).
+    constexpr int NSD = 2 * KC, NST = NSD + 4 * DT, LA = 4;
+    auto tile = [&](int t, auto sc) __attribute__((always_inline)) {
+        constexpr int S = decltype(sc)::value;
+        constexpr uint32_t KB = S * 2 * TILE, VB = KB + TILE;
+        const uint8_t *lds = smem;
+        const int k0 = t * kBwdTile;
+        u32x4 ra[NST], rb[NSD];
+        f32x16 sacc[2], pacc[2];
+        bf16x8 dsb[4];
+        auto read = [&](auto fc) __attribute__((always_inline)) {
+            constexpr int f = decltype(fc)::value;
+            if constexpr (f < NSD) {
+                constexpr int kt = f / KC, kc = f % KC;
+                ra[f] = lds16(lds + KB + kt * 32 * ROW + rowo[kc]);
+                rb[f] = lds16(lds + VB + kt * 32 * ROW + rowo[kc]);
+            } else if constexpr (f < NST) {
+                constexpr int ch = (f - NSD) / DT, dt = (f - NSD) % DT;
+                const u32x2 a0 = lds_tr(lds + KB + 16 * ch * ROW + tro[0][dt]);
+                const u32x2 a1 = lds_tr(lds + KB + 16 * ch * ROW + tro[1][dt]);
+                ra[f] = u32x4{a0[0], a0[1], a1[0], a1[1]};
+            }
+        };
+        // element 4a + b of half kt is key k0 + kt*32 + 8a + 4h + b
+        auto elem = [&](int kt, int i) __attribute__((always_inline)) {
+            const int key = k0 + kt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+            float p = exp2_hw(sacc[kt][i] * c + nlc);
+            if (key >= N || (CAUSAL && key > my_q)) p = 0.f;
+            dsb[2 * kt + (i >> 3)][i & 7] = (__bf16)(p * (pacc[kt][i] + nd));
+        };
+        static_for<LA>([&](auto fc) { read(fc); });
+        static_for<NST>([&](auto fc) {
+            constexpr int f = decltype(fc)::value;
+            read(std::integral_constant<int, f + LA>{});
+            if constexpr (f < NSD) {
+                constexpr int kt = f / KC, kc = f % KC;
+                if constexpr (kc == 0) {
+                    sacc[kt] = mfma(ra[f], qr[kc], f32x16{});
+                    pacc[kt] = mfma(rb[f], dor[kc], f32x16{});
+                } else {
+                    sacc[kt] = mfma(ra[f], qr[kc], sacc[kt]);
+                    pacc[kt] = mfma(rb[f], dor[kc], pacc[kt]);
+                }
+            } else {
+                constexpr int ch = (f - NSD) / DT, dt = (f - NSD) % DT;
+                dq[dt] = mfma(ra[f], __builtin_bit_cast(u32x4, dsb[ch]), dq[dt]);
+            }
+            constexpr int EPS = 16 / KC;
+            if constexpr (f >= KC && f < 2 * KC) {
+#pragma unroll
+                for (int i = (f - KC) * EPS; i < (f - KC + 1) * EPS; ++i) elem(0, i);
+            }
+            if constexpr (f >= NSD && f < NSD + KC) {
+#pragma unroll
+                for (int i = (f - NSD) * EPS; i < (f - NSD + 1) * EPS; ++i) elem(1, i);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+
+    // two tiles per loop iteration (constant LDS stages, one path for the
+    // accumulators); causal tiles past the wave's queries are masked
+    auto step = [&](int t, auto sc) __attribute__((always_inline)) {
+        constexpr int S = decltype(sc)::value;
+        if (t + 1 < n_kt) issue(t + 1, S ^ 1);
+        tile(t, sc);
+        wait_vm_n<0>();
+        __syncthreads();
+    };
+    issue(0, 0);
+    wait_vm_n<0>();
+    __syncthreads();
+    int t = 0;
+    for (; t + 1 < n_kt; t += 2) {
+        step(t, std::integral_constant<int, 0>{});
+        step(t + 1, std::integral_constant<int, 1>{});
+    }
+    if (t < n_kt) step(t, std::integral_constant<int, 0>{});
 
     if (my_q < N) {
         uint16_t *dqp = dQ + head + (size_t)my_q * D;
@@ -380,7 +508,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_t(const void *q, const void *k, const void *v, const void *o, const float *lse,
                         const void *dout, void *dq, void *dk, void *dv, int BH, int N, float scale,
-                        float *dlt, hipStream_t stream)
+                        float *ws, hipStream_t stream)
 {
     const auto *Q = static_cast<const uint16_t *>(q), *K = static_cast<const uint16_t *>(k);
     const auto *V = static_cast<const uint16_t *>(v), *O = static_cast<const uint16_t *>(o);
@@ -388,13 +516,13 @@ hipError_t launch_bwd_t(const void *q, const void *k, const void *v, const void 
     const long rows = (long)BH * N;
     const long dot_threads = rows * (D / 8);
     hipLaunchKernelGGL((bwd_dot_kernel<D>), dim3((unsigned)((dot_threads + kBwdThreads - 1) / kBwdThreads)),
-                       dim3(kBwdThreads), 0, stream, O, G, dlt, rows);
+                       dim3(kBwdThreads), 0, stream, O, G, lse, ws, rows, 1.f / scale);
     const int nb = (N + kBwdBlock - 1) / kBwdBlock;
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(nb * BH)), dim3(kBwdThreads), 0, stream,
-                       Q, K, V, G, lse, dlt, static_cast<uint16_t *>(dk), static_cast<uint16_t *>(dv), N, BH,
-                       scale);
+                       Q, K, V, G, ws, ws + rows, static_cast<uint16_t *>(dk), static_cast<uint16_t *>(dv), N,
+                       BH, scale);
     hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(nb * BH)), dim3(kBwdThreads), 0, stream,
-                       Q, K, V, G, lse, dlt, static_cast<uint16_t *>(dq), N, BH, nb, scale);
+                       Q, K, V, G, ws, ws + rows, static_cast<uint16_t *>(dq), N, BH, nb, scale);
     return hipGetLastError();
 }
 

@@ -18,8 +18,8 @@ hipError_t launch_fwd_fp8(const uint8_t *q8, const uint8_t *k8, const uint8_t *v
                           const float *qs, const float *ks, const float *vs, void *o, float *lse,
                           int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
 
-// Backward: fp32 D_i = dO_i . O_i of every row is the only workspace.
-inline size_t bwd_workspace_bytes(int B, int H, int N) { return (size_t)B * H * N * sizeof(float); }
+// Backward workspace: per row -L_i / scale, then per row -D_i (D_i = dO_i . O_i), fp32.
+inline size_t bwd_workspace_bytes(int B, int H, int N) { return 2 * (size_t)B * H * N * sizeof(float); }
 
 hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const void *o,
                            const float *lse, const void *dout, void *dq, void *dk, void *dv, int B,

@@ -46,6 +46,7 @@
 // P is not quantised to E4M3: with V outliers of tens, a 3-bit mantissa on P
 // would exceed this path's accuracy bound.
 #include "fa_device.h"
+#include "fa_dma.h"
 #include "fa_launch.h"
 
 #include <type_traits>
@@ -68,71 +69,6 @@ __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w, bool hi) {
     const bf16x2 r = hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
                         : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
     return __builtin_bit_cast(uint32_t, r);
-}
-
-// Plain buffer descriptor (base, no stride, num_records = bytes, raw access):
-// reads past `bytes` return zeros. Built in SGPRs for use in inline asm.
-__device__ __forceinline__ u32x4 sgpr_rsrc(const void *base, uint32_t bytes) {
-    const uint64_t a = (uint64_t)base;
-    u32x4 r;
-    r[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
-    r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
-    r[2] = __builtin_amdgcn_readfirstlane(bytes);
-    r[3] = 0x00020000u;
-    return r;
-}
-
-// The tile copies below are issued as inline asm and tracked by hand with
-// explicit vmcnt waits: the compiler treats its own LDS-DMA intrinsic as a
-// store that may alias every later LDS read and would wait for all of them,
-// which would serialise the prefetch ring.
-
-// 16-byte global -> LDS copy per lane: lane l writes lds_addr + 16 l
-// (an SALU write of M0 needs one wait state before an LDS-DMA reads it)
-__device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :: "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
-}
-// the same with the LDS address given as an SGPR base plus a constant
-template <uint32_t IMM>
-__device__ __forceinline__ void dma16c(u32x4 rsrc, uint32_t lds_base, uint32_t voff, uint32_t soff) {
-    asm volatile("s_add_u32 m0, %0, %4\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :: "s"(lds_base), "v"(voff), "s"(rsrc), "s"(soff), "n"(IMM) : "memory");
-}
-// 16- and 8-byte global -> register loads whose completion is also tracked by hand
-__device__ __forceinline__ u32x4 vload16(u32x4 rsrc, uint32_t voff, uint32_t soff) {
-    u32x4 v;
-    asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen" : "=v"(v) : "v"(voff), "s"(rsrc), "s"(soff) : "memory");
-    return v;
-}
-__device__ __forceinline__ u32x2 vload8(u32x4 rsrc, uint32_t voff, uint32_t soff) {
-    u32x2 v;
-    asm volatile("buffer_load_dwordx2 %0, %1, %2, %3 offen" : "=v"(v) : "v"(voff), "s"(rsrc), "s"(soff) : "memory");
-    return v;
-}
-
-// wait until at most n vector-memory operations of this wave are outstanding
-template <int n>
-__device__ __forceinline__ void wait_vm_n() {
-    static_assert(n >= 0 && n < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(n) : "memory");
-}
-__device__ __forceinline__ void wait_vm(int n) {
-    switch (n) {
-    case 0: wait_vm_n<0>(); break;
-    case 1: wait_vm_n<1>(); break;
-    case 2: wait_vm_n<2>(); break;
-    case 3: wait_vm_n<3>(); break;
-    case 4: wait_vm_n<4>(); break;
-    case 5: wait_vm_n<5>(); break;
-    case 6: wait_vm_n<6>(); break;
-    case 7: wait_vm_n<7>(); break;
-    default: wait_vm_n<8>(); break;
-    }
-}
-// workgroup barrier that orders LDS only (no wait on outstanding global loads)
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // ---------------------------------------------------------------------------
@@ -162,14 +98,6 @@ __device__ __forceinline__ void lds_barrier() {
 constexpr int kThreads3 = 256;
 constexpr int kRing = 4;    // LDS stages of K and of V
 
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
-    (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F &&f) {
-    static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
 
 template <int OFF> __device__ __forceinline__ u32x4 ds_b128(uint32_t a) {
     u32x4 r;

@@ -79,8 +79,9 @@ fa_status fa_fwd_fp8(const uint8_t *q8, const uint8_t *k8, const uint8_t *v8,
                      float scale, int causal, void *stream);
 
 /*
- * Bytes of device workspace fa_bwd needs (fp32 D_i = dO_i . O_i of every row:
- * B * H * N * 4). Returns 0 for unsupported sizes.
+ * Bytes of device workspace fa_bwd needs (two fp32 values per row: -L_i/scale
+ * and -D_i with D_i = dO_i . O_i; B * H * N * 8). Returns 0 for unsupported
+ * sizes.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
 

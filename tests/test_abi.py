@@ -88,7 +88,7 @@ def test_fp8_validation(lib):
 
 def test_bwd_validation(lib):
     need = lib.fa_bwd_workspace_bytes(2, 4, 1000, 128)
-    assert need == 2 * 4 * 1000 * 4          # fp32 D per row
+    assert need == 2 * 4 * 1000 * 8          # fp32 -L/scale and -D per row
     assert lib.fa_bwd_workspace_bytes(2, 4, 1000, 96) == 0
     assert lib.fa_bwd_workspace_bytes(0, 4, 1000, 128) == 0
 
