@@ -215,8 +215,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     // end of steps KC - 1 and NSD - 1), and P/dS written by VALU are read by
     // an MFMA at least a step later.
     constexpr int NSD = 2 * KC, NST = NSD + 4 * DT, LA = 4;
-    auto tile = [&](int t, auto sc) __attribute__((always_inline)) {
+    auto tile = [&](int t, auto sc, auto mc) __attribute__((always_inline)) {
         constexpr int S = decltype(sc)::value;
+        constexpr bool MASKED = decltype(mc)::value;
         constexpr uint32_t QB = S * 2 * TILE, DB = QB + TILE;   // stage bases in LDS
         const uint8_t *lds = smem;
         const float *rows = reinterpret_cast<const float *>(smem + ROWS + S * 2 * kBwdTile * 4);
@@ -255,7 +256,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
         };
         auto elem = [&](int qt, int i) __attribute__((always_inline)) {
             float p = exp2_hw(sacc[qt][i] * c);
-            if (CAUSAL && my_key > q0 + qt * 32 + 8 * (i >> 2) + 4 * h + (i & 3)) p = 0.f;
+            if (MASKED && my_key > q0 + qt * 32 + 8 * (i >> 2) + 4 * h + (i & 3)) p = 0.f;
             pb[2 * qt + (i >> 3)][i & 7] = (__bf16)p;
             dsb[2 * qt + (i >> 3)][i & 7] = (__bf16)(p * pacc[qt][i]);
         };
@@ -290,14 +291,19 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
         for (int k = 0; k < 4; ++k) asm volatile("" : "+v"(pb[k]), "+v"(dsb[k]));
     };
 
-    // Two tiles per loop iteration, so that the LDS stages are constants and
-    // the accumulators follow one path through the loop (causal tiles whose
-    // queries all precede the wave's keys are computed and masked; a wave
-    // meets at most one).
-    auto step = [&](int t, auto sc) __attribute__((always_inline)) {
+    // Tile t uses LDS stage (t - t0) & 1. The causal mask is only needed on
+    // the two tiles that meet this block's keys (computed first; a wave whose
+    // keys all follow a tile's queries gets zeros from it). The rest run two
+    // per loop iteration, so that the stages are constants and the
+    // accumulators follow one path through the loop.
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using Plain = std::false_type;
+    using Masked = std::true_type;
+    auto step = [&](int t, auto sc, auto mc) __attribute__((always_inline)) {
         constexpr int S = decltype(sc)::value;
         if (t + 1 < n_qt) issue(t + 1, S ^ 1);
-        tile(t, sc);
+        tile(t, sc, mc);
         wait_vm_n<0>();
         __syncthreads();
     };
@@ -305,11 +311,16 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     wait_vm_n<0>();
     __syncthreads();
     int t = t0;
-    for (; t + 1 < n_qt; t += 2) {
-        step(t, std::integral_constant<int, 0>{});
-        step(t + 1, std::integral_constant<int, 1>{});
+    if constexpr (CAUSAL) {
+        step(t0, S0{}, Masked{});
+        if (t0 + 1 < n_qt) step(t0 + 1, S1{}, Masked{});
+        t = t0 + 2;
     }
-    if (t < n_qt) step(t, std::integral_constant<int, 0>{});
+    for (; t + 1 < n_qt; t += 2) {
+        step(t, S0{}, Plain{});
+        step(t + 1, S1{}, Plain{});
+    }
+    if (t < n_qt) step(t, S0{}, Plain{});
 
     // the last MFMAs wrote dK^T / dV^T: cover the MFMA-write -> read distance
     // (the pins after the nops keep the reads of the accumulators below them)
@@ -414,8 +425,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
     //   dS of kt = 0 is formed during steps [KC, 2 KC), of kt = 1 during the
     //   first 2 DT dQ steps (which only use kt = 0).
     constexpr int NSD = 2 * KC, NST = NSD + 4 * DT, LA = 4;
-    auto tile = [&](int t, auto sc) __attribute__((always_inline)) {
+    auto tile = [&](int t, auto sc, auto mc) __attribute__((always_inline)) {
         constexpr int S = decltype(sc)::value;
+        constexpr bool MASKED = decltype(mc)::value;
         constexpr uint32_t KB = S * 2 * TILE, VB = KB + TILE;
         const uint8_t *lds = smem;
         const int k0 = t * kBwdTile;
@@ -439,7 +451,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
         auto elem = [&](int kt, int i) __attribute__((always_inline)) {
             const int key = k0 + kt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
             float p = exp2_hw(sacc[kt][i] * c + nlc);
-            if (key >= N || (CAUSAL && key > my_q)) p = 0.f;
+            if (MASKED && (key >= N || (CAUSAL && key > my_q))) p = 0.f;
             dsb[2 * kt + (i >> 3)][i & 7] = (__bf16)(p * (pacc[kt][i] + nd));
         };
         static_for<LA>([&](auto fc) { read(fc); });
@@ -472,24 +484,35 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
         });
     };
 
-    // two tiles per loop iteration (constant LDS stages, one path for the
-    // accumulators); causal tiles past the wave's queries are masked
-    auto step = [&](int t, auto sc) __attribute__((always_inline)) {
+    // Tile t uses LDS stage t & 1. Only the last tiles need the mask: the
+    // two that meet this block's queries (causal) and the one holding key N.
+    // The others run two per loop iteration (constant stages, one path for
+    // the accumulators); the masked ones follow.
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using Plain = std::false_type;
+    using Masked = std::true_type;
+    auto step = [&](int t, auto sc, auto mc) __attribute__((always_inline)) {
         constexpr int S = decltype(sc)::value;
         if (t + 1 < n_kt) issue(t + 1, S ^ 1);
-        tile(t, sc);
+        tile(t, sc, mc);
         wait_vm_n<0>();
         __syncthreads();
     };
+    const int n_plain = CAUSAL ? min(n_kt, 2 * qb) : (N % kBwdTile ? n_kt - 1 : n_kt);
     issue(0, 0);
     wait_vm_n<0>();
     __syncthreads();
     int t = 0;
-    for (; t + 1 < n_kt; t += 2) {
-        step(t, std::integral_constant<int, 0>{});
-        step(t + 1, std::integral_constant<int, 1>{});
+    for (; t + 1 < n_plain; t += 2) {
+        step(t, S0{}, Plain{});
+        step(t + 1, S1{}, Plain{});
     }
-    if (t < n_kt) step(t, std::integral_constant<int, 0>{});
+    if (t < n_plain) step(t++, S0{}, Plain{});
+    for (; t < n_kt; ++t) {
+        if (t & 1) step(t, S1{}, Masked{});
+        else step(t, S0{}, Masked{});
+    }
 
     if (my_q < N) {
         uint16_t *dqp = dQ + head + (size_t)my_q * D;
