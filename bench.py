@@ -275,7 +275,7 @@ def main():
                               "workload": "causal bf16 backward B1 H32 N16384 d128",
                               "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS,
                                            "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
-                                           "traffic": None,
+                                           "traffic": measured_traffic("pmc_bwd_causal_B1H32N16384d128.md"),
                                            "kernel": "bwd_dot + bwd_dkdv + bwd_dq kernels"}}
     if result["value"] is None and "decode" in result:
         result["value"], result["unit"] = result["decode"]["value"], "GB/s"
