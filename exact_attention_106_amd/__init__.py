@@ -9,6 +9,7 @@ first call does, and raises if it has not been built.
 """
 from __future__ import annotations
 
+import ctypes
 import math
 from typing import Optional, Tuple
 
@@ -18,8 +19,8 @@ from . import _lib
 from ._lib import FaError
 
 __all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_bwd", "fa_bwd_workspace_bytes",
-           "fa_paged_decode", "fa_paged_decode_workspace_bytes", "fa_status_str", "fa_version",
-           "FaError"]
+           "fa_paged_decode", "fa_paged_decode_workspace_bytes", "BlockManager", "fa_copy_pages",
+           "fa_status_str", "fa_version", "FaError"]
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -207,6 +208,70 @@ def fa_paged_decode(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
                                      workspace.numel(), _stream(q))
     _lib.check(st, "fa_paged_decode")
     return out, lse
+
+
+class BlockManager:
+    """Paged KV block manager of libfa.so (fa_bm_*): on-demand pages, shared
+    pages with reference counts, copy-on-write. The state is a host buffer
+    owned by this object; every method is one library call."""
+
+    def __init__(self, num_pages: int, max_seqs: int, max_blocks_per_seq: int, page_size: int = 16):
+        lib = _lib.load()
+        nbytes = int(lib.fa_bm_state_bytes(num_pages, max_seqs, max_blocks_per_seq))
+        if nbytes == 0:
+            raise ValueError("num_pages, max_seqs and max_blocks_per_seq must be positive")
+        self._buf = ctypes.create_string_buffer(nbytes)
+        self.num_pages, self.max_seqs, self.max_blocks, self.page_size = (
+            num_pages, max_seqs, max_blocks_per_seq, page_size)
+        _lib.check(lib.fa_bm_init(self._buf, nbytes, num_pages, max_seqs, max_blocks_per_seq, page_size),
+                   "fa_bm_init")
+
+    def add_seq(self, seq: int, num_tokens: int) -> None:
+        _lib.check(_lib.load().fa_bm_add_seq(self._buf, seq, num_tokens), "fa_bm_add_seq")
+
+    def fork(self, parent: int, child: int) -> None:
+        _lib.check(_lib.load().fa_bm_fork(self._buf, parent, child), "fa_bm_fork")
+
+    def append_token(self, seq: int) -> Tuple[int, int]:
+        """Reserve one more token of seq; returns (src, dst) pages to copy first, or (-1, -1)."""
+        src, dst = ctypes.c_int32(-1), ctypes.c_int32(-1)
+        _lib.check(_lib.load().fa_bm_append_token(self._buf, seq, ctypes.byref(src), ctypes.byref(dst)),
+                   "fa_bm_append_token")
+        return src.value, dst.value
+
+    def free_seq(self, seq: int) -> None:
+        _lib.check(_lib.load().fa_bm_free_seq(self._buf, seq), "fa_bm_free_seq")
+
+    def num_free_pages(self) -> int:
+        return int(_lib.load().fa_bm_num_free_pages(self._buf))
+
+    def seq_len(self, seq: int) -> int:
+        return int(_lib.load().fa_bm_seq_len(self._buf, seq))
+
+    def refcount(self, page: int) -> int:
+        return int(_lib.load().fa_bm_page_refcount(self._buf, page))
+
+    def block_table(self) -> Tuple[torch.Tensor, torch.Tensor]:
+        """(block_table int32 [max_seqs, max_blocks], ctx_lens int32 [max_seqs]) on the host."""
+        table = torch.empty((self.max_seqs, self.max_blocks), dtype=torch.int32)
+        ctx = torch.empty((self.max_seqs,), dtype=torch.int32)
+        _lib.check(_lib.load().fa_bm_block_table(self._buf, _ptr(table), _ptr(ctx)), "fa_bm_block_table")
+        return table, ctx
+
+
+def fa_copy_pages(kcache: torch.Tensor, vcache: torch.Tensor, src: torch.Tensor, dst: torch.Tensor) -> None:
+    """Copy pages src[i] -> dst[i] of both caches (bf16 [P, H, page_size, d]); src, dst device int32 [n]."""
+    _check_dev("kcache", kcache, torch.bfloat16)
+    if kcache.dim() != 4:
+        raise ValueError("kcache must be [P, H, page_size, d]")
+    _check_dev("vcache", vcache, torch.bfloat16, kcache.shape)
+    n = src.numel()
+    _check_dev("src", src, torch.int32, (n,))
+    _check_dev("dst", dst, torch.int32, (n,))
+    P, H, ps, d = kcache.shape
+    st = _lib.load().fa_copy_pages(_ptr(kcache), _ptr(vcache), _ptr(src), _ptr(dst), n, P, H, d, ps,
+                                   _stream(kcache))
+    _lib.check(st, "fa_copy_pages")
 
 
 def fa_status_str(status: int) -> str:

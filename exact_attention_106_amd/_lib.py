@@ -11,11 +11,14 @@ LIB_PATH = os.path.join(PKG, "libfa.so")
 FA_OK = 0
 STATUS_NAMES = {
     0: "FA_OK", 1: "FA_ERR_NULL_PTR", 2: "FA_ERR_BAD_SHAPE", 3: "FA_ERR_UNSUPPORTED",
-    4: "FA_ERR_WORKSPACE", 5: "FA_ERR_HIP",
+    4: "FA_ERR_WORKSPACE", 5: "FA_ERR_HIP", 6: "FA_ERR_NO_PAGES", 7: "FA_ERR_STATE",
 }
 # every symbol include/fa.h declares
 EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_bwd_workspace_bytes", "fa_bwd",
-           "fa_paged_decode_workspace_bytes", "fa_paged_decode", "fa_status_str", "fa_version")
+           "fa_paged_decode_workspace_bytes", "fa_paged_decode", "fa_bm_state_bytes", "fa_bm_init",
+           "fa_bm_add_seq", "fa_bm_fork", "fa_bm_append_token", "fa_bm_free_seq",
+           "fa_bm_num_free_pages", "fa_bm_seq_len", "fa_bm_page_refcount", "fa_bm_block_table",
+           "fa_copy_pages", "fa_status_str", "fa_version")
 
 
 class FaError(RuntimeError):
@@ -52,6 +55,29 @@ def load() -> ctypes.CDLL:
         lib.fa_paged_decode_workspace_bytes.restype = sz
         lib.fa_paged_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
         lib.fa_paged_decode.restype = i
+        ip = ctypes.POINTER(ctypes.c_int32)
+        lib.fa_bm_state_bytes.argtypes = [i, i, i]
+        lib.fa_bm_state_bytes.restype = sz
+        lib.fa_bm_init.argtypes = [vp, sz, i, i, i, i]
+        lib.fa_bm_init.restype = i
+        lib.fa_bm_add_seq.argtypes = [vp, i, i]
+        lib.fa_bm_add_seq.restype = i
+        lib.fa_bm_fork.argtypes = [vp, i, i]
+        lib.fa_bm_fork.restype = i
+        lib.fa_bm_append_token.argtypes = [vp, i, ip, ip]
+        lib.fa_bm_append_token.restype = i
+        lib.fa_bm_free_seq.argtypes = [vp, i]
+        lib.fa_bm_free_seq.restype = i
+        lib.fa_bm_num_free_pages.argtypes = [vp]
+        lib.fa_bm_num_free_pages.restype = i
+        lib.fa_bm_seq_len.argtypes = [vp, i]
+        lib.fa_bm_seq_len.restype = i
+        lib.fa_bm_page_refcount.argtypes = [vp, i]
+        lib.fa_bm_page_refcount.restype = i
+        lib.fa_bm_block_table.argtypes = [vp, vp, vp]
+        lib.fa_bm_block_table.restype = i
+        lib.fa_copy_pages.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp]
+        lib.fa_copy_pages.restype = i
         lib.fa_status_str.argtypes = [i]
         lib.fa_status_str.restype = ctypes.c_char_p
         lib.fa_version.argtypes = []

@@ -122,6 +122,8 @@ const char *fa_status_str(fa_status s)
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head size, page size, flag or scale not supported";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace too small";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported an error";
+    case FA_ERR_NO_PAGES: return "FA_ERR_NO_PAGES: the block manager has no free page";
+    case FA_ERR_STATE: return "FA_ERR_STATE: invalid block-manager state or sequence id in the wrong state";
     }
     return "unknown fa_status";
 }

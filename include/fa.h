@@ -40,7 +40,10 @@ typedef enum fa_status {
     FA_ERR_BAD_SHAPE = 2,    /* a size is <= 0 or out of the supported range */
     FA_ERR_UNSUPPORTED = 3,  /* head size / page size / flag value not supported */
     FA_ERR_WORKSPACE = 4,    /* workspace too small */
-    FA_ERR_HIP = 5           /* the HIP runtime reported an error at launch */
+    FA_ERR_HIP = 5,          /* the HIP runtime reported an error at launch */
+    FA_ERR_NO_PAGES = 6,     /* block manager: no free page left */
+    FA_ERR_STATE = 7         /* block manager: invalid state, or the sequence is
+                                absent / already present */
 } fa_status;
 
 /*
@@ -143,6 +146,52 @@ fa_status fa_paged_decode(const void *q, const void *kcache, const void *vcache,
                           int page_size, int max_blocks_per_seq, int num_pages,
                           float scale, void *workspace, size_t workspace_bytes,
                           void *stream);
+
+/*
+ * Paged KV block manager (PagedAttention, "FlashAttention系列优化": logical
+ * blocks of a sequence map to physical pages through a block table; pages are
+ * taken on demand; sequences share pages with reference counts and
+ * copy-on-write). Host-side bookkeeping only: the state lives in host memory
+ * the caller provides (fa_bm_state_bytes), the library allocates nothing, and
+ * the only device work is fa_copy_pages. A failed call returns its status and
+ * changes nothing. Not thread-safe for one state; separate states are
+ * independent.
+ *   fa_bm_init:         empty pool of num_pages pages of page_size tokens for
+ *                       sequence ids 0..max_seqs-1 of up to max_blocks_per_seq
+ *                       blocks each
+ *   fa_bm_add_seq:      a new sequence of num_tokens tokens on fresh pages
+ *   fa_bm_fork:         child maps every block of parent (refcounts + 1)
+ *   fa_bm_append_token: reserve the slot of one more token of seq: a fresh page
+ *                       when the token starts a block; when its block's page is
+ *                       shared, seq gets a private page and (*cow_src,
+ *                       *cow_dst) name the page to copy (fa_copy_pages) before
+ *                       the token's K/V are written; otherwise both are -1
+ *   fa_bm_free_seq:     drop seq's references; pages reaching 0 are free again
+ *   fa_bm_block_table:  host block_table [max_seqs, max_blocks_per_seq] (-1
+ *                       padded) and ctx_lens [max_seqs] (0 for absent ids), the
+ *                       arguments of fa_paged_decode / fa_paged_prefill once
+ *                       copied to the device
+ */
+size_t fa_bm_state_bytes(int num_pages, int max_seqs, int max_blocks_per_seq);
+fa_status fa_bm_init(void *state, size_t state_bytes, int num_pages, int max_seqs,
+                     int max_blocks_per_seq, int page_size);
+fa_status fa_bm_add_seq(void *state, int seq, int num_tokens);
+fa_status fa_bm_fork(void *state, int parent, int child);
+fa_status fa_bm_append_token(void *state, int seq, int32_t *cow_src, int32_t *cow_dst);
+fa_status fa_bm_free_seq(void *state, int seq);
+int fa_bm_num_free_pages(const void *state);          /* -1 for an invalid state */
+int fa_bm_seq_len(const void *state, int seq);        /* -1 for an absent sequence */
+int fa_bm_page_refcount(const void *state, int page); /* -1 for a bad page id */
+fa_status fa_bm_block_table(const void *state, int32_t *block_table, int32_t *ctx_lens);
+
+/*
+ * Copy n whole pages (every head, page_size tokens, d channels, bf16) of both
+ * caches [num_pages, H, page_size, d]: page src[i] -> page dst[i]. src, dst:
+ * device int32 [n], ids in [0, num_pages) (not checked on the device), no dst
+ * repeated and no dst among the src. The copies of copy-on-write.
+ */
+fa_status fa_copy_pages(void *kcache, void *vcache, const int32_t *src, const int32_t *dst, int n,
+                        int num_pages, int H, int d, int page_size, void *stream);
 
 /* Human-readable name of a status (static string, never NULL). */
 const char *fa_status_str(fa_status s);
