@@ -19,7 +19,8 @@ from . import _lib
 from ._lib import FaError
 
 __all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_bwd", "fa_bwd_workspace_bytes",
-           "fa_paged_decode", "fa_paged_decode_workspace_bytes", "BlockManager", "fa_copy_pages",
+           "fa_paged_decode", "fa_paged_decode_workspace_bytes", "fa_paged_prefill", "BlockManager",
+           "fa_copy_pages",
            "fa_status_str", "fa_version", "FaError"]
 
 
@@ -207,6 +208,40 @@ def fa_paged_decode(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
                                      max_blocks, P, scale, _ptr(workspace),
                                      workspace.numel(), _stream(q))
     _lib.check(st, "fa_paged_decode")
+    return out, lse
+
+
+def fa_paged_prefill(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
+                     block_table: torch.Tensor, ctx_lens: torch.Tensor, scale: Optional[float] = None,
+                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                     return_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Paged (chunked) prefill. q bf16 [S, H, n_new, d]: the n_new newest tokens of each
+    sequence (positions ctx_lens[s] - n_new ..), attending causally to the paged cache."""
+    _check_dev("q", q, torch.bfloat16)
+    if q.dim() != 4:
+        raise ValueError("q must be [S, H, n_new, d]")
+    S, H, n_new, d = q.shape
+    _check_dev("kcache", kcache, torch.bfloat16)
+    if kcache.dim() != 4 or kcache.shape[1] != H or kcache.shape[3] != d:
+        raise ValueError("kcache must be [P, H, page_size, d]")
+    _check_dev("vcache", vcache, torch.bfloat16, kcache.shape)
+    P, _, page_size, _ = kcache.shape
+    _check_dev("block_table", block_table, torch.int32)
+    if block_table.dim() != 2 or block_table.shape[0] != S:
+        raise ValueError("block_table must be [S, max_blocks]")
+    _check_dev("ctx_lens", ctx_lens, torch.int32, (S,))
+    if out is None:
+        out = torch.empty((S, H, n_new, d), dtype=torch.bfloat16, device=q.device)
+    _check_dev("out", out, torch.bfloat16, (S, H, n_new, d))
+    if lse is None and return_lse:
+        lse = torch.empty((S, H, n_new), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check_dev("lse", lse, torch.float32, (S, H, n_new))
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = _lib.load().fa_paged_prefill(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(block_table),
+                                      _ptr(ctx_lens), _ptr(out), _ptr(lse), S, H, n_new, d, page_size,
+                                      block_table.shape[1], P, scale, _stream(q))
+    _lib.check(st, "fa_paged_prefill")
     return out, lse
 
 

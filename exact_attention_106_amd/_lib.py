@@ -15,7 +15,8 @@ STATUS_NAMES = {
 }
 # every symbol include/fa.h declares
 EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_bwd_workspace_bytes", "fa_bwd",
-           "fa_paged_decode_workspace_bytes", "fa_paged_decode", "fa_bm_state_bytes", "fa_bm_init",
+           "fa_paged_decode_workspace_bytes", "fa_paged_decode", "fa_paged_prefill",
+           "fa_bm_state_bytes", "fa_bm_init",
            "fa_bm_add_seq", "fa_bm_fork", "fa_bm_append_token", "fa_bm_free_seq",
            "fa_bm_num_free_pages", "fa_bm_seq_len", "fa_bm_page_refcount", "fa_bm_block_table",
            "fa_copy_pages", "fa_status_str", "fa_version")
@@ -55,6 +56,8 @@ def load() -> ctypes.CDLL:
         lib.fa_paged_decode_workspace_bytes.restype = sz
         lib.fa_paged_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
         lib.fa_paged_decode.restype = i
+        lib.fa_paged_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+        lib.fa_paged_prefill.restype = i
         ip = ctypes.POINTER(ctypes.c_int32)
         lib.fa_bm_state_bytes.argtypes = [i, i, i]
         lib.fa_bm_state_bytes.restype = sz

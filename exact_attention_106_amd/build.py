@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ["api.hip", "fwd_f32.hip", "fwd_prefill.hip", "decode.hip", "bwd.hip", "block_manager.hip"]
+SOURCES = ["api.hip", "fwd_f32.hip", "fwd_prefill.hip", "decode.hip", "bwd.hip", "block_manager.hip",
+           "paged_prefill.hip"]
 ARCH = "gfx950"
 
 

@@ -113,6 +113,25 @@ fa_status fa_paged_decode(const void *q, const void *kcache, const void *vcache,
                                             static_cast<hipStream_t>(stream)));
 }
 
+fa_status fa_paged_prefill(const void *q, const void *kcache, const void *vcache,
+                           const int32_t *block_table, const int32_t *ctx_lens, void *o, float *lse,
+                           int num_seqs, int H, int n_new, int d, int page_size,
+                           int max_blocks_per_seq, int num_pages, float scale, void *stream)
+{
+    if (!q || !kcache || !vcache || !block_table || !ctx_lens || !o) return FA_ERR_NULL_PTR;
+    if (num_seqs <= 0 || H <= 0 || n_new <= 0 || d <= 0 || page_size <= 0 || max_blocks_per_seq <= 0 ||
+        num_pages <= 0)
+        return FA_ERR_BAD_SHAPE;
+    if (d != 128 || page_size != 16) return FA_ERR_UNSUPPORTED;
+    if ((long long)num_seqs * H > 65535) return FA_ERR_BAD_SHAPE;
+    if ((long long)num_seqs * H * n_new * d > kMaxElems) return FA_ERR_BAD_SHAPE;
+    if ((long long)max_blocks_per_seq * page_size > kMaxElems) return FA_ERR_BAD_SHAPE;
+    if (bad_scale(scale)) return FA_ERR_UNSUPPORTED;
+    return from_hip(fa::launch_paged_prefill(q, kcache, vcache, block_table, ctx_lens, o, lse, num_seqs, H,
+                                             n_new, max_blocks_per_seq, scale,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 const char *fa_status_str(fa_status s)
 {
     switch (s) {

@@ -48,6 +48,11 @@ inline size_t decode_workspace_bytes(int num_seqs, int H, int max_blocks_per_seq
            sizeof(int);
 }
 
+hipError_t launch_paged_prefill(const void *q, const void *kcache, const void *vcache,
+                                const int32_t *block_table, const int32_t *ctx_lens, void *o,
+                                float *lse, int num_seqs, int H, int n_new, int max_blocks_per_seq,
+                                float scale, hipStream_t stream);
+
 hipError_t launch_paged_decode(const void *q, const void *kcache, const void *vcache,
                                const int32_t *block_table, const int32_t *ctx_lens, void *o,
                                float *lse, int num_seqs, int H, int d, int page_size,

@@ -148,6 +148,23 @@ fa_status fa_paged_decode(const void *q, const void *kcache, const void *vcache,
                           void *stream);
 
 /*
+ * Paged (chunked) prefill: the n_new newest tokens of each sequence attend to
+ * its paged KV cache (PagedAttention block table, "FlashAttention系列优化";
+ * the tile loop of the FlashAttention-2 forward of the same page). Query i of
+ * sequence s is the token at position ctx_lens[s] - n_new + i and sees cached
+ * tokens 0 .. that position (causal); its own K/V must already be in the
+ * cache. A query whose position is negative sees nothing (O = 0, L = -inf).
+ *   q:        bf16 [num_seqs, H, n_new, d]
+ *   kcache, vcache, block_table, ctx_lens: as for fa_paged_decode
+ *   o:        bf16 [num_seqs, H, n_new, d];  lse: fp32 [num_seqs, H, n_new] or NULL
+ * d == 128, page_size == 16, num_seqs * H <= 65535.
+ */
+fa_status fa_paged_prefill(const void *q, const void *kcache, const void *vcache,
+                           const int32_t *block_table, const int32_t *ctx_lens, void *o, float *lse,
+                           int num_seqs, int H, int n_new, int d, int page_size,
+                           int max_blocks_per_seq, int num_pages, float scale, void *stream);
+
+/*
  * Paged KV block manager (PagedAttention, "FlashAttention系列优化": logical
  * blocks of a sequence map to physical pages through a block table; pages are
  * taken on demand; sequences share pages with reference counts and

@@ -183,3 +183,33 @@ def attention_bwd(q, k, v, dout, scale: float, causal: bool):
     if rc != 0:
         raise RuntimeError("oracle_attention_bwd failed")
     return dq, dk, dv
+
+
+def paged_prefill(q, kcache_bits, vcache_bits, block_table, ctx_lens, scale: float):
+    """Chunked prefill through a block table (PagedAttention block table of
+    "FlashAttention系列优化"): query i of sequence s is the token at position
+    ctx_s - n_new + i and attends to the sequence's tokens 0..position. Token t
+    of sequence s lives in page block_table[s][t // page_size], slot
+    t % page_size. q [S, H, n_new, d]; caches bf16 bit patterns [P, H, ps, d].
+    Returns (o [S, H, n_new, d], lse [S, H, n_new]) in fp64."""
+    q = _f64(q)
+    kc = np.asarray(kcache_bits, dtype=np.uint16)
+    vc = np.asarray(vcache_bits, dtype=np.uint16)
+    bt = np.asarray(block_table, dtype=np.int64)
+    cl = np.asarray(ctx_lens, dtype=np.int64)
+    s_, h, n_new, d = q.shape
+    ps = kc.shape[2]
+    o = np.empty((s_, h, n_new, d), dtype=np.float64)
+    lse = np.empty((s_, h, n_new), dtype=np.float64)
+    for s in range(s_):
+        ctx = int(cl[s])
+        t = np.arange(ctx)
+        pages, slots = bt[s, t // ps], t % ps
+        pos = (ctx - n_new + np.arange(n_new)).astype(np.int64)
+        for hh in range(h):
+            k = bf16_bits_to_f64(kc[pages, hh, slots, :])
+            v = bf16_bits_to_f64(vc[pages, hh, slots, :])
+            o[s, hh], lse[s, hh] = attention_rows(q[s, hh], pos, k.reshape(ctx, d), v.reshape(ctx, d),
+                                                  scale, True)
+    return o, lse
+
