@@ -7,6 +7,8 @@ One step = one pass of the whole path over resident synthetic inputs:
   4. fa_bwd      backward of (1) given its O, L and a seeded dO (the first
                  of the next rows; TFLOP/s on the 5-product count, 2.5x the
                  forward's)
+  5. fa_paged_prefill  chunked prefill through the block table: the last
+                 2048 tokens of 16 sequences (contexts 2048..16384), H=32, d=128
 Each launch is bracketed by HIP events on the stream it runs on. `value` is
 the prefill's TFLOP/s (4*B*H*N^2*d, halved for causal, per the kernel's mean
 event time); decode GB/s and fp8 TFLOP/s are reported beside it. The CPU
@@ -138,7 +140,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--only", default="", help="comma list of prefill,fp8,decode,backward (default all)")
+    ap.add_argument("--only", default="", help="comma list of prefill,fp8,decode,backward,paged_prefill (default all)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -152,7 +154,7 @@ def main():
     import exact_attention_106_amd as fa
     from exact_attention_106_amd import inputs
 
-    only = set(filter(None, args.only.split(","))) or {"prefill", "fp8", "decode", "backward"}
+    only = set(filter(None, args.only.split(","))) or {"prefill", "fp8", "decode", "backward", "paged_prefill"}
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     fa.fa_version()
@@ -192,6 +194,12 @@ def main():
         dq3, dk3, dv3 = (torch.empty_like(q3) for _ in range(3))
         parts.append(("backward", lambda: fa.fa_bwd(q3, k3, v3, o3, l3, g3, scale=x3.scale, causal=True,
                                                     workspace=wsb, dq=dq3, dk=dk3, dv=dv3)))
+    if "paged_prefill" in only:
+        p6 = inputs.paged_prefill_workload(device=dev)
+        o6 = torch.empty(p6.q.shape, dtype=torch.bfloat16, device=dev)
+        l6 = torch.empty(p6.q.shape[:3], dtype=torch.float32, device=dev)
+        parts.append(("paged_prefill", lambda: fa.fa_paged_prefill(p6.q, p6.kcache, p6.vcache, p6.block_table,
+                                                                   p6.ctx_lens, scale=p6.scale, out=o6, lse=l6)))
     torch.cuda.synchronize()
 
     log("warmup %d" % args.warmup)
@@ -277,6 +285,21 @@ def main():
                                            "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
                                            "traffic": measured_traffic("pmc_bwd_causal_B1H32N16384d128.md"),
                                            "kernel": "bwd_dot + bwd_dkdv + bwd_dq kernels"}}
+    if "paged_prefill" in ms:
+        n_new = p6.q.shape[2]
+        ctx = p6.ctx_lens.cpu().double()
+        # sum over sequences and new tokens of 4 d (position + 1), times heads
+        keys = (n_new * (ctx - n_new) + n_new * (n_new + 1) / 2).sum().item()
+        f = 4.0 * 128 * 32 * keys
+        tf = f / (ms["paged_prefill"] * 1e-3) / 1e12
+        result["paged_prefill"] = {"value": tf, "unit": "TFLOP/s", "launch_ms": ms["paged_prefill"],
+                                   "launch_ms_spread": spread("paged_prefill"), "flop_per_launch": f,
+                                   "workload": "paged chunked prefill S16 H32 d128, last 2048 tokens of "
+                                               "contexts 2048..16384",
+                                   "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS,
+                                                "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
+                                                "traffic": measured_traffic("pmc_paged_prefill_S16H32d128.md"),
+                                                "kernel": "paged_prefill_kernel"}}
     if result["value"] is None and "decode" in result:
         result["value"], result["unit"] = result["decode"]["value"], "GB/s"
     if not args.no_cpu_baseline and "prefill" in only:

@@ -244,6 +244,18 @@ def paged_pool(num_seqs: int, H: int, d: int, ctx_lo: int, ctx_hi: int, seed: in
                  meta={"ctx_lo": ctx_lo, "ctx_hi": ctx_hi, "seed": seed, "share": share})
 
 
+def paged_prefill_workload(device="cpu") -> Paged:
+    """Chunked prefill through a block table: 16 sequences, H = 32, d = 128,
+    contexts U{2048..16384} (PCG64(7)), shared prefixes and a shuffled pool as
+    for the decode workload; q holds the last 2048 tokens of every sequence
+    [16, 32, 2048, 128] (PCG64(8), N(0,1) -> bf16)."""
+    p = paged_pool(16, 32, 128, 2048, 16384, seed=7, device=device, name="paged_prefill_S16H32d128")
+    rng = np.random.Generator(np.random.PCG64(8))
+    q = torch.from_numpy(rng.standard_normal((16, 32, 2048, 128), dtype=np.float32)).to(torch.bfloat16)
+    p.q = q.to(device)
+    return p
+
+
 def config5(device="cpu") -> Paged:
     return paged_pool(64, 32, 128, 512, 32768, seed=5, device=device,
                       name="paged_decode_S64H32d128_ctx512-32768")

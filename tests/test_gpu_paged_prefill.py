@@ -118,3 +118,27 @@ def test_copy_pages_exact(gpu):
     for a, b in zip(src.tolist(), dst.tolist()):
         ek[b], ev[b] = k0[a], v0[a]
     assert torch.equal(kc, ek) and torch.equal(vc, ev)
+
+
+def test_paged_prefill_workload_sampled(gpu):
+    """The benchmark's workload (16 sequences, H = 32, last 2048 tokens of
+    contexts 2048..16384) on sampled (sequence, head, token) rows."""
+    p = inputs.paged_prefill_workload(device=gpu)
+    log("fa_paged_prefill workload S16 H32 n_new=2048 (sampled rows)")
+    o, l = fa.fa_paged_prefill(p.q, p.kcache, p.vcache, p.block_table, p.ctx_lens, scale=p.scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    bt, cl = p.block_table.cpu().numpy(), p.ctx_lens.cpu().numpy()
+    n_new = p.q.shape[2]
+    for s, h in zip(rng.integers(0, 16, 6), rng.integers(0, 32, 6)):
+        ctx = int(cl[s])
+        t = np.arange(ctx)
+        pages = torch.from_numpy(bt[s, t // 16].astype(np.int64)).to(gpu)
+        slots = torch.from_numpy(t % 16).to(gpu)
+        k = p.kcache[pages, int(h), slots]
+        v = p.vcache[pages, int(h), slots]
+        rows = np.sort(rng.choice(n_new, 8, replace=False))
+        rows[0], rows[-1] = 0, n_new - 1
+        pos = ctx - n_new + rows
+        ro, rl = oracle.attention_rows(f64(p.q[s, h][rows]), pos, f64(k), f64(v), p.scale, True)
+        check("workload s%d h%d" % (s, h), o[s, h][rows], l[s, h][rows], ro, rl)
