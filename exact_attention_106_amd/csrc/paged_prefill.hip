@@ -11,8 +11,8 @@
 // tokens 0..p. Workgroup = 4 waves x 32 queries of one (sequence, head); grid
 // (ceil(n_new / 128), S * H), last query blocks (most keys) first. A tile is
 // 64 keys = 4 pages: wave w copies page 4t + w of K and of V straight from the
-// cache into LDS (1 KiB pieces, rows swizzled) while the previous tile is
-// computed. Orientation as in the prefill kernel: S^T = K Q^T with the wave's
+// cache into LDS (1 KiB pieces, rows swizzled) two tiles ahead of the compute,
+// through three LDS stages. Orientation as in the prefill kernel: S^T = K Q^T with the wave's
 // queries as columns (one query per lane, so the softmax is in-lane plus one
 // exchange between the wave halves), O^T += V^T P^T with V^T read transposed
 // from LDS. Slots past ctx_s in the last page may hold anything: their scores
@@ -38,9 +38,11 @@ __global__ __launch_bounds__(kPpThreads, 1) void paged_prefill_kernel(
     constexpr int D = 128, ROW = 2 * D, CPR = D / 8, KC = D / 16, DT = D / 32;
     constexpr int TILE = kPpTile * ROW;              // 16 KiB of K or V
     constexpr int PAGE = kPpPage * ROW;              // one (page, head): 4 KiB
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TILE];   // [stage][K, V]
+    constexpr int STAGES = 3;                         // tile copies run two tiles ahead
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * 2 * TILE];   // [stage][K, V]
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, h = lane >> 5;
+    const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: table reads are scalar
     const int sh = blockIdx.y;
     const int s = sh / H, hd = sh % H;
     const int qb = gridDim.x - 1 - blockIdx.x;
@@ -83,10 +85,15 @@ __global__ __launch_bounds__(kPpThreads, 1) void paged_prefill_kernel(
         src_off[i] = (uint32_t)((4 * i + (lane >> 4)) * ROW + ((pc ^ swz<CPR>(r)) << 4));
     }
     const uint32_t lds0 = (uint32_t)(size_t)smem;
-    auto issue = [&](int t, int st) __attribute__((always_inline)) {
+    // the page of tile t + 2 is looked up in the block table one step before
+    // its copy is issued, so the lookup's latency hides behind a tile
+    auto page_of = [&](int t) __attribute__((always_inline)) {
         const int blk = t * 4 + w;
-        if (blk < n_pages) {
-            const int32_t pid = __builtin_amdgcn_readfirstlane(bt[blk]);
+        return blk < n_pages ? __builtin_amdgcn_readfirstlane(bt[blk]) : -1;
+    };
+    // returns the number of copies issued (8, or 0 past the table)
+    auto issue = [&](int pid, int st) __attribute__((always_inline)) {
+        if (pid >= 0) {
             const size_t off = (size_t)pid * page_stride + head_page;
             const u32x4 rk = sgpr_rsrc(Kc + off, PAGE), rv = sgpr_rsrc(Vc + off, PAGE);
             const uint32_t base = __builtin_amdgcn_readfirstlane(lds0 + st * 2 * TILE + w * PAGE);
@@ -96,6 +103,7 @@ __global__ __launch_bounds__(kPpThreads, 1) void paged_prefill_kernel(
                 dma16(rv, base + TILE + i * 1024, src_off[i], 0);
             }
         }
+        return pid >= 0;
     };
 
     f32x16 oacc[DT];
@@ -201,25 +209,36 @@ __global__ __launch_bounds__(kPpThreads, 1) void paged_prefill_kernel(
     };
     // tiles entirely at or below the wave's first position need no mask
     const int wave_p0 = base_pos + qw;
+    // Tile t uses LDS stage t mod 3. The step of tile t issues the copies of
+    // tile t + 2 (its page looked up during the step before), looks up the
+    // page of tile t + 3, and ends once tile t + 1 is in LDS.
+    int pid_next = -1;
     auto step = [&](int t, auto sc) __attribute__((always_inline)) {
         constexpr int S = decltype(sc)::value;
-        if (t + 1 < n_kt) issue(t + 1, S ^ 1);
+        const bool ahead = t + 2 < n_kt && issue(pid_next, (S + 2) % STAGES);
+        pid_next = t + 3 < n_kt ? page_of(t + 3) : -1;
         zero_tail(t, S);
         if (t * kPpTile + kPpTile - 1 <= wave_p0) tile(t, sc, std::false_type{});
         else tile(t, sc, std::true_type{});
-        wait_vm_n<0>();
+        if (ahead) wait_vm_n<8>();
+        else wait_vm_n<0>();
         __syncthreads();
     };
     if (n_kt > 0) {
-        issue(0, 0);
-        wait_vm_n<0>();
+        issue(page_of(0), 0);
+        bool ahead = 1 < n_kt && issue(page_of(1), 1);
+        pid_next = 2 < n_kt ? page_of(2) : -1;
+        if (ahead) wait_vm_n<8>();
+        else wait_vm_n<0>();
         __syncthreads();
         int t = 0;
-        for (; t + 1 < n_kt; t += 2) {
+        for (; t + 2 < n_kt; t += 3) {
             step(t, std::integral_constant<int, 0>{});
             step(t + 1, std::integral_constant<int, 1>{});
+            step(t + 2, std::integral_constant<int, 2>{});
         }
         if (t < n_kt) step(t, std::integral_constant<int, 0>{});
+        if (t + 1 < n_kt) step(t + 1, std::integral_constant<int, 1>{});
     }
 
     // epilogue: O = O~ / l (rows of this lane's query), L = (m + log2 l) ln 2
