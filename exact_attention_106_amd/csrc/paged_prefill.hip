@@ -9,7 +9,7 @@
 //
 // Query i of sequence s sits at position p = ctx_s - n_new + i and sees cached
 // tokens 0..p. Workgroup = 4 waves x 32 queries of one (sequence, head); grid
-// (ceil(n_new / 128), S * H), last query blocks (most keys) first. A tile is
+// ceil(n_new / 128) * S * H, XCD-aware (below), last query blocks first. A tile is
 // 64 keys = 4 pages: wave w copies page 4t + w of K and of V straight from the
 // cache into LDS (1 KiB pieces, rows swizzled) two tiles ahead of the compute,
 // through three LDS stages. Orientation as in the prefill kernel: S^T = K Q^T with the wave's
@@ -33,7 +33,7 @@ constexpr int kPpPage = 16;     // tokens per page
 __global__ __launch_bounds__(kPpThreads, 1) void paged_prefill_kernel(
     const uint16_t *__restrict__ Q, const uint8_t *__restrict__ Kc, const uint8_t *__restrict__ Vc,
     const int32_t *__restrict__ BT, const int32_t *__restrict__ CTX, uint16_t *__restrict__ O,
-    float *__restrict__ LSE, int SH, int H, int n_new, int max_blocks, float scale)
+    float *__restrict__ LSE, int SH, int H, int n_new, int n_qb, int max_blocks, float scale)
 {
     constexpr int D = 128, ROW = 2 * D, CPR = D / 8, KC = D / 16, DT = D / 32;
     constexpr int TILE = kPpTile * ROW;              // 16 KiB of K or V
@@ -43,9 +43,21 @@ __global__ __launch_bounds__(kPpThreads, 1) void paged_prefill_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: table reads are scalar
-    const int sh = blockIdx.y;
+    // Workgroup ids go round-robin over the 8 XCDs. When S*H is a multiple of
+    // 8, all query blocks of one (sequence, head) get ids of one residue mod 8
+    // and consecutive ids on it, so they run together on one XCD and read
+    // the same K/V pages through its L2; each head's blocks run heaviest first.
+    int sh, rank;
+    if (SH % 8 == 0) {
+        const int x = blockIdx.x % 8, j = blockIdx.x / 8;
+        rank = j % n_qb;
+        sh = 8 * (j / n_qb) + x;
+    } else {
+        rank = blockIdx.x / SH;
+        sh = blockIdx.x % SH;
+    }
     const int s = sh / H, hd = sh % H;
-    const int qb = gridDim.x - 1 - blockIdx.x;
+    const int qb = n_qb - 1 - rank;
     const int ctx = CTX[s];
     const int base_pos = ctx - n_new;                 // position of query 0
     const int qw = qb * kPpBlock + 32 * w;            // first query of the wave
@@ -266,11 +278,11 @@ hipError_t launch_paged_prefill(const void *q, const void *kcache, const void *v
                                 float *lse, int num_seqs, int H, int n_new, int max_blocks_per_seq,
                                 float scale, hipStream_t stream)
 {
-    const dim3 grid((unsigned)((n_new + kPpBlock - 1) / kPpBlock), (unsigned)(num_seqs * H));
-    hipLaunchKernelGGL(paged_prefill_kernel, grid, dim3(kPpThreads), 0, stream,
+    const int n_qb = (n_new + kPpBlock - 1) / kPpBlock;
+    hipLaunchKernelGGL(paged_prefill_kernel, dim3((unsigned)(n_qb * num_seqs * H)), dim3(kPpThreads), 0, stream,
                        static_cast<const uint16_t *>(q), static_cast<const uint8_t *>(kcache),
                        static_cast<const uint8_t *>(vcache), block_table, ctx_lens,
-                       static_cast<uint16_t *>(o), lse, num_seqs * H, H, n_new, max_blocks_per_seq, scale);
+                       static_cast<uint16_t *>(o), lse, num_seqs * H, H, n_new, n_qb, max_blocks_per_seq, scale);
     return hipGetLastError();
 }
 
