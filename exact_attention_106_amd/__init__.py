@@ -18,7 +18,7 @@ import torch
 from . import _lib
 from ._lib import FaError
 
-__all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_bwd", "fa_bwd_workspace_bytes",
+__all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_fwd_block_sparse", "fa_bwd", "fa_bwd_workspace_bytes",
            "fa_paged_decode", "fa_paged_decode_workspace_bytes", "fa_paged_prefill", "BlockManager",
            "fa_copy_pages",
            "fa_status_str", "fa_version", "FaError"]
@@ -128,6 +128,28 @@ def fa_fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, q_scale: to
                                 _ptr(v_scale), _ptr(out), _ptr(lse), B, H, N, d, scale,
                                 int(bool(causal)), _stream(q8))
     _lib.check(st, "fa_fwd_fp8")
+    return out, lse
+
+
+def fa_fwd_block_sparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: torch.Tensor,
+                        scale: Optional[float] = None, causal: bool = False, dropout_p: float = 0.0,
+                        seed: int = 0, out: Optional[torch.Tensor] = None,
+                        lse: Optional[torch.Tensor] = None, return_lse: bool = True
+                        ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Block-sparse bf16 attention forward (128 x 128 blocks, d = 128) with optional
+    dropout. block_mask: device uint8 (or bool) [ceil(N/128), ceil(N/128)]."""
+    B, H, N, d, out = _dense_common(q, k, v, torch.bfloat16, out, lse, torch.bfloat16)
+    if block_mask.dtype == torch.bool:
+        block_mask = block_mask.to(torch.uint8)
+    nb = (N + 127) // 128
+    _check_dev("block_mask", block_mask, torch.uint8, (nb, nb))
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = _lib.load().fa_fwd_block_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(block_mask), _ptr(out), _ptr(lse),
+                                         B, H, N, d, scale, int(bool(causal)), float(dropout_p),
+                                         int(seed) & 0xFFFFFFFFFFFFFFFF, _stream(q))
+    _lib.check(st, "fa_fwd_block_sparse")
     return out, lse
 
 

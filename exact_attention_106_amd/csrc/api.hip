@@ -60,6 +60,20 @@ fa_status fa_fwd_fp8(const uint8_t *q8, const uint8_t *k8, const uint8_t *v8, co
                                        scale, causal, static_cast<hipStream_t>(stream)));
 }
 
+fa_status fa_fwd_block_sparse(const void *q, const void *k, const void *v, const uint8_t *block_mask,
+                              void *o, float *lse, int B, int H, int N, int d, float scale, int causal,
+                              float dropout_p, uint64_t seed, void *stream)
+{
+    fa_status st = check_dense(q, k, v, o, B, H, N, d, scale, causal);
+    if (st != FA_OK) return st;
+    if (!block_mask) return FA_ERR_NULL_PTR;
+    if (d != 128) return FA_ERR_UNSUPPORTED;
+    if (N > 131072) return FA_ERR_BAD_SHAPE;
+    if (!(dropout_p >= 0.f && dropout_p < 1.f)) return FA_ERR_UNSUPPORTED;
+    return from_hip(fa::launch_fwd_block_sparse(q, k, v, block_mask, o, lse, B, H, N, scale, causal, dropout_p,
+                                                seed, static_cast<hipStream_t>(stream)));
+}
+
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d)
 {
     if (B <= 0 || H <= 0 || N <= 0 || (d != 64 && d != 128)) return 0;

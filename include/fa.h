@@ -82,6 +82,28 @@ fa_status fa_fwd_fp8(const uint8_t *q8, const uint8_t *k8, const uint8_t *v8,
                      float scale, int causal, void *stream);
 
 /*
+ * Block-sparse attention forward with optional dropout, bf16 (d == 128).
+ * Block-sparse FlashAttention (91haoming.cn FlashAttention v1-v3 article, v1
+ * results): the fused tile loop runs only over the (query block, key block)
+ * pairs that block_mask keeps; blocks are 128 x 128 tokens.
+ *   block_mask: device uint8 [nb, nb], nb = ceil(N / 128), shared by every
+ *     batch and head; entry [i][j] != 0 keeps key block j for query block i.
+ *     With causal != 0, keys after the query are masked as well. A query with
+ *     no kept key gets O = 0 and L = -inf.
+ *   dropout_p in [0, 1): each softmax weight P_ij is kept with probability
+ *     1 - dropout_p and scaled by 1 / (1 - dropout_p) (the "masking and
+ *     dropout" fused into the kernel, same article); L and the normaliser are
+ *     those before dropout. The decision uses Philox4x32-10 (Salmon et al.,
+ *     SC 2011) with key (seed & 0xffffffff, seed >> 32) and counter
+ *     (j / 4, i, b * H + h, 0): P_ij is dropped iff word j % 4 of the output
+ *     is below floor(dropout_p * 2^32).
+ * Other arguments as for fa_fwd; N <= 131072.
+ */
+fa_status fa_fwd_block_sparse(const void *q, const void *k, const void *v, const uint8_t *block_mask,
+                              void *o, float *lse, int B, int H, int N, int d, float scale, int causal,
+                              float dropout_p, uint64_t seed, void *stream);
+
+/*
  * Bytes of device workspace fa_bwd needs (two fp32 values per row: -L_i/scale
  * and -D_i with D_i = dO_i . O_i; B * H * N * 8). Returns 0 for unsupported
  * sizes.

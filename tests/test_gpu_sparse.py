@@ -1,0 +1,69 @@
+"""GPU parity of the block-sparse attention forward with dropout
+(fa_fwd_block_sparse through the C ABI) against the fp64 oracle
+(oracle/sparse.py). Tolerances as for the bf16 forward: O max-abs 2e-2 (with
+dropout the weights are scaled by 1 / (1 - p), so the bound is 2e-2 / (1 - p)),
+L 1e-3. Keep decisions are integer work and must agree exactly; a single
+disagreement would move O far beyond the bound."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import sparse
+import exact_attention_106_amd as fa
+from exact_attention_106_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def f64(t):
+    return oracle.bf16_bits_to_f64(t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16))
+
+
+def check(name, o, l, ro, rl, tol_o):
+    got_o, got_l = f64(o), l.cpu().double().numpy()
+    assert np.all(np.isfinite(got_o)), name + ": non-finite O"
+    fin = np.isfinite(rl)
+    assert np.array_equal(np.isfinite(got_l), fin), name + ": L finiteness"
+    eo = float(np.max(np.abs(got_o - ro)))
+    el = float(np.max(np.abs(got_l[fin] - rl[fin]))) if fin.any() else 0.0
+    log("%s: max|dO|=%.3e max|dL|=%.3e" % (name, eo, el))
+    assert eo <= tol_o and el <= 1e-3
+
+
+@pytest.mark.parametrize("B,H,N,causal,density,p_drop", [
+    (1, 2, 64, False, 1.0, 0.0), (1, 2, 200, True, 0.6, 0.0), (2, 1, 1000, False, 0.5, 0.0),
+    (1, 3, 1500, True, 0.4, 0.0), (1, 2, 700, False, 0.5, 0.1), (1, 2, 1030, True, 0.7, 0.5),
+    (2, 2, 333, True, 1.0, 0.25)])
+def test_block_sparse(gpu, B, H, N, causal, density, p_drop):
+    x = inputs.dense(B, H, N, 128, seed=900 + N)
+    nb = (N + 127) // 128
+    rng = np.random.default_rng(N)
+    mask = (rng.random((nb, nb)) < density).astype(np.uint8)
+    if nb > 2:
+        mask[1, :] = 0                                   # a block row that keeps nothing
+    seed = 0x1234_5678_9ABC_DEF0 + N
+    log("fa_fwd_block_sparse B%d H%d N%d causal=%d density=%.1f p=%.2f" % (B, H, N, causal, density, p_drop))
+    o, l = fa.fa_fwd_block_sparse(x.q.to(gpu), x.k.to(gpu), x.v.to(gpu), torch.from_numpy(mask).to(gpu),
+                                  scale=x.scale, causal=causal, dropout_p=p_drop, seed=seed)
+    torch.cuda.synchronize()
+    ro, rl = sparse.block_sparse_attention(f64(x.q), f64(x.k), f64(x.v), mask, x.scale, causal,
+                                           p_drop=p_drop, seed=seed)
+    check("sparse N%d c%d p%.2f" % (N, causal, p_drop), o, l, ro, rl, 2e-2 / (1 - p_drop))
+
+
+def test_block_sparse_full_mask_matches_fa_fwd(gpu):
+    x = inputs.dense(1, 2, 1000, 128, seed=950)
+    q, k, v = x.q.to(gpu), x.k.to(gpu), x.v.to(gpu)
+    mask = torch.ones((8, 8), dtype=torch.uint8, device=gpu)
+    o1, l1 = fa.fa_fwd_block_sparse(q, k, v, mask, scale=x.scale, causal=True)
+    o2, l2 = fa.fa_fwd(q, k, v, scale=x.scale, causal=True)
+    torch.cuda.synchronize()
+    assert float((o1.float() - o2.float()).abs().max()) < 2e-2
+    assert float((l1 - l2).abs().max()) < 1e-3
