@@ -9,6 +9,9 @@ One step = one pass of the whole path over resident synthetic inputs:
                  forward's)
   5. fa_paged_prefill  chunked prefill through the block table: the last
                  2048 tokens of 16 sequences (contexts 2048..16384), H=32, d=128
+  6. fa_fwd_block_sparse  the inputs of (1) with a seeded block mask keeping
+                 half of the causal 128 x 128 blocks (the diagonal always),
+                 without and with dropout p = 0.1
 Each launch is bracketed by HIP events on the stream it runs on. `value` is
 the prefill's TFLOP/s (4*B*H*N^2*d, halved for causal, per the kernel's mean
 event time); decode GB/s and fp8 TFLOP/s are reported beside it. The CPU
@@ -25,6 +28,8 @@ import math
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -140,7 +145,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--only", default="", help="comma list of prefill,fp8,decode,backward,paged_prefill (default all)")
+    ap.add_argument("--only", default="",
+                    help="comma list of prefill,fp8,decode,backward,paged_prefill,block_sparse (default all)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -154,7 +160,8 @@ def main():
     import exact_attention_106_amd as fa
     from exact_attention_106_amd import inputs
 
-    only = set(filter(None, args.only.split(","))) or {"prefill", "fp8", "decode", "backward", "paged_prefill"}
+    only = set(filter(None, args.only.split(","))) or {"prefill", "fp8", "decode", "backward", "paged_prefill",
+                                                         "block_sparse"}
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     fa.fa_version()
@@ -200,6 +207,19 @@ def main():
         l6 = torch.empty(p6.q.shape[:3], dtype=torch.float32, device=dev)
         parts.append(("paged_prefill", lambda: fa.fa_paged_prefill(p6.q, p6.kcache, p6.vcache, p6.block_table,
                                                                    p6.ctx_lens, scale=p6.scale, out=o6, lse=l6)))
+    if "block_sparse" in only:
+        if "prefill" not in only and "backward" not in only:
+            x3 = inputs.config3()
+            q3, k3, v3 = x3.q.to(dev), x3.k.to(dev), x3.v.to(dev)
+        bmask = inputs.block_mask(16384, density=0.5, seed=9, causal=True)
+        bmask_d = bmask.to(dev)
+        o7 = torch.empty_like(q3)
+        l7 = torch.empty(q3.shape[:3], dtype=torch.float32, device=dev)
+        parts.append(("block_sparse", lambda: fa.fa_fwd_block_sparse(q3, k3, v3, bmask_d, scale=x3.scale, causal=True,
+                                                                     out=o7, lse=l7)))
+        parts.append(("block_sparse_dropout", lambda: fa.fa_fwd_block_sparse(q3, k3, v3, bmask_d, scale=x3.scale,
+                                                                             causal=True, dropout_p=0.1, seed=11,
+                                                                             out=o7, lse=l7)))
     torch.cuda.synchronize()
 
     log("warmup %d" % args.warmup)
@@ -300,6 +320,23 @@ def main():
                                                 "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
                                                 "traffic": measured_traffic("pmc_paged_prefill_S16H32d128.md"),
                                                 "kernel": "paged_prefill_kernel"}}
+    if "block_sparse" in ms:
+        nb = bmask.shape[0]
+        keep = bmask.numpy().astype(bool)
+        # visible (query, key) pairs: full off-diagonal kept blocks + causal diagonal blocks
+        i, j = np.nonzero(keep)
+        pairs = float(((i > j).sum()) * 128 * 128 + (i == j).sum() * 128 * 129 / 2)
+        f = 4.0 * 128 * 32 * pairs
+        for name in ("block_sparse", "block_sparse_dropout"):
+            tf = f / (ms[name] * 1e-3) / 1e12
+            result[name] = {"value": tf, "unit": "TFLOP/s", "launch_ms": ms[name],
+                            "launch_ms_spread": spread(name), "flop_per_launch": f,
+                            "workload": "block-sparse causal B1 H32 N16384 d128, %d of %d causal blocks kept%s"
+                                        % (int(keep.sum()), nb * (nb + 1) // 2,
+                                           ", dropout 0.1" if name.endswith("dropout") else ""),
+                            "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS,
+                                         "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS, "traffic": None,
+                                         "kernel": "sparse_fwd_kernel"}}
     if result["value"] is None and "decode" in result:
         result["value"], result["unit"] = result["decode"]["value"], "GB/s"
     if not args.no_cpu_baseline and "prefill" in only:

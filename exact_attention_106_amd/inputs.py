@@ -256,6 +256,19 @@ def paged_prefill_workload(device="cpu") -> Paged:
     return p
 
 
+def block_mask(N: int, density: float, seed: int, causal: bool = True) -> torch.Tensor:
+    """Seeded 128 x 128 block mask (uint8 [ceil(N/128)]^2) keeping a fraction
+    `density` of the blocks (of the causal ones when causal), the diagonal
+    always, so that every query keeps at least its own block."""
+    nb = (N + 127) // 128
+    rng = np.random.Generator(np.random.PCG64(seed))
+    m = rng.random((nb, nb)) < density
+    if causal:
+        m &= np.tril(np.ones((nb, nb), dtype=bool))
+    np.fill_diagonal(m, True)
+    return torch.from_numpy(m.astype(np.uint8))
+
+
 def config5(device="cpu") -> Paged:
     return paged_pool(64, 32, 128, 512, 32768, seed=5, device=device,
                       name="paged_decode_S64H32d128_ctx512-32768")
