@@ -8,7 +8,8 @@ nothing from the product: the two share no code.
 Every function here computes the plain definition of attention in fp64
 (scores, 3-pass safe softmax, weighted sum, logsumexp); see ``oracle.c`` for
 the passages each step follows. ``online.py`` holds the pages' tiled
-online-softmax algorithm, used only to pin this oracle against the pages.
+online-softmax algorithm, used only to pin this oracle against the pages;
+``sparse.py`` the block-sparse attention with dropout (numpy).
 """
 from __future__ import annotations
 
