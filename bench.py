@@ -146,7 +146,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--only", default="",
-                    help="comma list of prefill,fp8,decode,backward,paged_prefill,block_sparse (default all)")
+                    help="comma list of prefill,fp8,decode,backward,paged_prefill,block_sparse,"
+                         "fp8_quantize (default all)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -161,7 +162,7 @@ def main():
     from exact_attention_106_amd import inputs
 
     only = set(filter(None, args.only.split(","))) or {"prefill", "fp8", "decode", "backward", "paged_prefill",
-                                                         "block_sparse"}
+                                                         "block_sparse", "fp8_quantize"}
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     fa.fa_version()
@@ -220,6 +221,18 @@ def main():
         parts.append(("block_sparse_dropout", lambda: fa.fa_fwd_block_sparse(q3, k3, v3, bmask_d, scale=x3.scale,
                                                                              causal=True, dropout_p=0.1, seed=11,
                                                                              out=o7, lse=l7)))
+    if "fp8_quantize" in only:
+        # Q and K of the fp8 workload with the incoherent rotation, V without
+        qz = [inputs.quant_inputs(2, 16, 8192, 128, seed=40 + i) for i in range(3)]
+        xz = [x.to(dev) for x, _ in qz]
+        rz = qz[0][1].to(dev)
+        cz = [torch.empty(x.shape, dtype=torch.uint8, device=dev) for x in xz]
+        sz = [torch.empty((2, 16, 64), dtype=torch.float32, device=dev) for _ in xz]
+
+        def quantize_qkv():
+            for i, (x, rot) in enumerate(zip(xz, (rz, rz, None))):
+                fa.fa_quantize_fp8(x, rot, codes=cz[i], scales=sz[i])
+        parts.append(("fp8_quantize", quantize_qkv))
     torch.cuda.synchronize()
 
     log("warmup %d" % args.warmup)
@@ -337,6 +350,20 @@ def main():
                             "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS,
                                          "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS, "traffic": None,
                                          "kernel": "sparse_fwd_kernel"}}
+    if "fp8_quantize" in ms:
+        tokens = 2 * 16 * 8192
+        nbytes = tokens * 128 * (2 + 1) + 2 * 16 * 64 * 4      # bf16 in, E4M3 out, scales
+        per_launch = ms["fp8_quantize"] / 3
+        gbs = nbytes / (per_launch * 1e-3) / 1e9
+        result["fp8_quantize"] = {"value": 3 * tokens / (ms["fp8_quantize"] * 1e-3), "unit": "tokens/s",
+                                  "launch_ms": per_launch, "launch_ms_spread": spread("fp8_quantize"),
+                                  "bytes_per_launch": nbytes,
+                                  "workload": "rotate + E4M3 block quantise Q, K (Haar R) and V (no R), "
+                                              "B2 H16 N8192 d128 each, three launches",
+                                  "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
+                                               "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                                               "traffic": measured_traffic("pmc_fp8_quantize_B2H16N8192d128.md"),
+                                               "kernel": "fp8_quant_kernel"}}
     if result["value"] is None and "decode" in result:
         result["value"], result["unit"] = result["decode"]["value"], "GB/s"
     if not args.no_cpu_baseline and "prefill" in only:

@@ -18,7 +18,7 @@ import torch
 from . import _lib
 from ._lib import FaError
 
-__all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_fwd_block_sparse", "fa_bwd", "fa_bwd_workspace_bytes",
+__all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_quantize_fp8", "fa_fwd_block_sparse", "fa_bwd", "fa_bwd_workspace_bytes",
            "fa_paged_decode", "fa_paged_decode_workspace_bytes", "fa_paged_prefill", "BlockManager",
            "fa_copy_pages",
            "fa_status_str", "fa_version", "FaError"]
@@ -129,6 +129,33 @@ def fa_fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, q_scale: to
                                 int(bool(causal)), _stream(q8))
     _lib.check(st, "fa_fwd_fp8")
     return out, lse
+
+
+def fa_quantize_fp8(x: torch.Tensor, rot: Optional[torch.Tensor] = None,
+                    codes: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None
+                    ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Fused incoherent rotation + FP8 block quantisation of bf16 x [B, H, N, 128]:
+    y = x @ rot (rot bf16 [128, 128], or None for y = x), then per (b, h, 128-token
+    block) scale = max|y| / 448 and E4M3FN codes of y / scale (nearest even).
+    Returns (codes uint8 [B, H, N, 128], scales fp32 [B, H, ceil(N/128)]), the
+    layout fa_fwd_fp8 reads."""
+    _check_dev("x", x, torch.bfloat16)
+    if x.dim() != 4:
+        raise ValueError("x must be [B, H, N, d]")
+    B, H, N, d = x.shape
+    if rot is not None:
+        _check_dev("rot", rot, torch.bfloat16, (d, d))
+    if codes is None:
+        codes = torch.empty((B, H, N, d), dtype=torch.uint8, device=x.device)
+    codes = _as_u8("codes", codes)
+    _check_dev("codes", codes, torch.uint8, (B, H, N, d))
+    nsb = (N + 127) // 128
+    if scales is None:
+        scales = torch.empty((B, H, nsb), dtype=torch.float32, device=x.device)
+    _check_dev("scales", scales, torch.float32, (B, H, nsb))
+    st = _lib.load().fa_quantize_fp8(_ptr(x), _ptr(rot), _ptr(codes), _ptr(scales), B, H, N, d, _stream(x))
+    _lib.check(st, "fa_quantize_fp8")
+    return codes, scales
 
 
 def fa_fwd_block_sparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: torch.Tensor,

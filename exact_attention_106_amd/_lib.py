@@ -14,7 +14,7 @@ STATUS_NAMES = {
     4: "FA_ERR_WORKSPACE", 5: "FA_ERR_HIP", 6: "FA_ERR_NO_PAGES", 7: "FA_ERR_STATE",
 }
 # every symbol include/fa.h declares
-EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_fwd_block_sparse", "fa_bwd_workspace_bytes", "fa_bwd",
+EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_quantize_fp8", "fa_fwd_block_sparse", "fa_bwd_workspace_bytes", "fa_bwd",
            "fa_paged_decode_workspace_bytes", "fa_paged_decode", "fa_paged_prefill",
            "fa_bm_state_bytes", "fa_bm_init",
            "fa_bm_add_seq", "fa_bm_fork", "fa_bm_append_token", "fa_bm_free_seq",
@@ -56,6 +56,8 @@ def load() -> ctypes.CDLL:
         lib.fa_paged_decode_workspace_bytes.restype = sz
         lib.fa_paged_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
         lib.fa_paged_decode.restype = i
+        lib.fa_quantize_fp8.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
+        lib.fa_quantize_fp8.restype = i
         lib.fa_fwd_block_sparse.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, f, ctypes.c_uint64, vp]
         lib.fa_fwd_block_sparse.restype = i
         lib.fa_paged_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]

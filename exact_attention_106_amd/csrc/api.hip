@@ -60,6 +60,19 @@ fa_status fa_fwd_fp8(const uint8_t *q8, const uint8_t *k8, const uint8_t *v8, co
                                        scale, causal, static_cast<hipStream_t>(stream)));
 }
 
+fa_status fa_quantize_fp8(const void *x, const void *rot, uint8_t *codes, float *scales, int B, int H,
+                          int N, int d, void *stream)
+{
+    if (!x || !codes || !scales) return FA_ERR_NULL_PTR;
+    if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return FA_ERR_BAD_SHAPE;
+    if ((long long)B * H * N * d > kMaxElems) return FA_ERR_BAD_SHAPE;
+    if (d != 128) return FA_ERR_UNSUPPORTED;
+    const uintptr_t mis = reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(rot) |
+                          reinterpret_cast<uintptr_t>(codes);
+    if ((mis & 15) || (reinterpret_cast<uintptr_t>(scales) & 3)) return FA_ERR_UNSUPPORTED;
+    return from_hip(fa::launch_fp8_quantize(x, rot, codes, scales, B, H, N, static_cast<hipStream_t>(stream)));
+}
+
 fa_status fa_fwd_block_sparse(const void *q, const void *k, const void *v, const uint8_t *block_mask,
                               void *o, float *lse, int B, int H, int N, int d, float scale, int causal,
                               float dropout_p, uint64_t seed, void *stream)

@@ -48,6 +48,9 @@ inline size_t decode_workspace_bytes(int num_seqs, int H, int max_blocks_per_seq
            sizeof(int);
 }
 
+hipError_t launch_fp8_quantize(const void *x, const void *rot, uint8_t *codes, float *scales, int B, int H,
+                               int N, hipStream_t stream);
+
 hipError_t launch_fwd_block_sparse(const void *q, const void *k, const void *v, const uint8_t *block_mask,
                                    void *o, float *lse, int B, int H, int N, float scale, int causal,
                                    float dropout_p, uint64_t seed, hipStream_t stream);

@@ -186,6 +186,21 @@ def fp8_inputs(B: int, H: int, N: int, d: int, seed: int, outlier_frac: float = 
                name=name or f"fp8_B{B}H{H}N{N}d{d}")
 
 
+def quant_inputs(B: int, H: int, N: int, d: int, seed: int, outlier_frac: float = 0.001,
+                 outlier_mult: float = 20.0, device="cpu"):
+    """bf16 x [B, H, N, d] (N(0,1) with a fraction of entries scaled up as
+    outliers, as in fp8_inputs before rotation) and a bf16 Haar rotation [d, d]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.standard_normal((B, H, N, d), dtype=np.float32)
+    n_out = int(round(outlier_frac * x.size))
+    if n_out:
+        idx = rng.choice(x.size, size=n_out, replace=False)
+        x.reshape(-1)[idx] *= np.float32(outlier_mult)
+    r = haar_orthogonal(rng, d).astype(np.float32)
+    return (torch.from_numpy(x).to(torch.bfloat16).to(device),
+            torch.from_numpy(r).to(torch.bfloat16).to(device))
+
+
 def config4(device="cpu") -> Fp8:
     return fp8_inputs(2, 16, 8192, 128, seed=4, causal=True, device=device,
                       name="causal_fp8_B2H16N8192d128")

@@ -82,6 +82,26 @@ fa_status fa_fwd_fp8(const uint8_t *q8, const uint8_t *k8, const uint8_t *v8,
                      float scale, int causal, void *stream);
 
 /*
+ * Fused incoherent processing and FP8 block quantisation: the producer of
+ * fa_fwd_fp8's inputs (FlashAttention-3 FP8: "FlashAttention系列优化",
+ * FlashAttentionV3 / FP低精度, where Q and K are multiplied by a random
+ * orthogonal matrix before block quantisation so that outliers spread; the
+ * scores (QR)(KR)^T = QK^T do not change).
+ *   x: bf16 [B, H, N, d], device; rot: bf16 [d, d] row-major R, or NULL for
+ *     no rotation (V, or Q and K without incoherent processing);
+ *   codes: uint8 [B, H, N, d], OCP E4M3FN; scales: fp32 [B, H, ceil(N/128)].
+ *   With y = x R (fp32 sums of exact bf16 products), for each 128-token block
+ *   of each (b, h): scale = max |y| / 448 over the block (1 if that is 0) and
+ *   code = E4M3FN(clamp(y / scale, -448, 448)), rounded to nearest even.
+ *   The last block of a row may be short; it is scaled on its own tokens.
+ * d == 128; x, rot and codes 16-byte aligned, scales 4-byte aligned
+ * (FA_ERR_UNSUPPORTED otherwise); x must be finite. Device pointers; the
+ * call is asynchronous on stream.
+ */
+fa_status fa_quantize_fp8(const void *x, const void *rot, uint8_t *codes, float *scales, int B, int H,
+                          int N, int d, void *stream);
+
+/*
  * Block-sparse attention forward with optional dropout, bf16 (d == 128).
  * Block-sparse FlashAttention (91haoming.cn FlashAttention v1-v3 article, v1
  * results): the fused tile loop runs only over the (query block, key block)

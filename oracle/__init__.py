@@ -9,7 +9,8 @@ Every function here computes the plain definition of attention in fp64
 (scores, 3-pass safe softmax, weighted sum, logsumexp); see ``oracle.c`` for
 the passages each step follows. ``online.py`` holds the pages' tiled
 online-softmax algorithm, used only to pin this oracle against the pages;
-``sparse.py`` the block-sparse attention with dropout (numpy).
+``sparse.py`` the block-sparse attention with dropout (numpy); ``quant.py``
+the incoherent rotation and FP8 block quantisation (numpy).
 """
 from __future__ import annotations
 

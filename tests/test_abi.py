@@ -134,3 +134,17 @@ def test_binding_fails_loudly_without_device_tensors():
     q = torch.zeros(1, 1, 16, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.fa_fwd(q, q, q)
+
+
+def test_quantize_validation(lib):
+    f = lib.fa_quantize_fp8
+    call = lambda x=FAKE, r=None, c=FAKE, s=FAKE, B=1, H=1, N=16, d=128: f(x, r, c, s, B, H, N, d, None)
+    assert call(x=None) == NULL_PTR
+    assert call(c=None) == NULL_PTR
+    assert call(s=None) == NULL_PTR
+    assert call(N=0) == BAD_SHAPE
+    assert call(B=-1) == BAD_SHAPE
+    assert call(d=64) == UNSUPPORTED
+    assert call(x=FAKE + 8) == UNSUPPORTED          # 16-byte alignment
+    assert call(r=FAKE + 2) == UNSUPPORTED
+    assert call(s=FAKE + 2) == UNSUPPORTED

@@ -1,0 +1,138 @@
+"""GPU parity of the fused rotation + FP8 block quantiser (fa_quantize_fp8
+through the C ABI) against the fp64 oracle (oracle/quant.py).
+
+Tolerance, derived from the arithmetic: the kernel's y = x R is a sum of 128
+exact products of bf16 values in fp32, so |y_gpu - y| <= 128 * 2^-24 *
+sum_k |x_k| |R_kn| (the standard bound for recursive summation; computed per
+element below). The scale s = max|y| / 448 then agrees to that bound of the
+block's largest element plus one fp32 rounding. A code must be the nearest
+E4M3 value of y / s up to that slack: |decode(code) - y/s| <= half an E4M3 step
+at |y/s| + the slack carried into y/s (and the fp32 rounding of the
+division). Codes are integers: where y / s is farther than that slack from
+every rounding midpoint the code is unique and must match the oracle's
+exactly; elsewhere either neighbour is valid. Without a rotation y = x is
+exact and the scales match bit for bit, so only the division's own rounding
+is left.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import quant
+import exact_attention_106_amd as fa
+from exact_attention_106_amd import inputs
+
+pytestmark = pytest.mark.gpu
+U = 2.0 ** -24
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def f64(t):
+    return oracle.bf16_bits_to_f64(t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16))
+
+
+def check(name, x, r, codes, scales):
+    xd = f64(x)
+    rd = None if r is None else f64(r)
+    c_o, s_o, y_o = quant.rotate_quantize(xd, rd)
+    c_g = codes.cpu().numpy()
+    s_g = scales.cpu().double().numpy()
+    B, H, N, d = xd.shape
+    nb = (N + 127) // 128
+    # per-element bound on |y_gpu - y|
+    ey = 128 * U * (np.abs(xd) @ np.abs(rd)) if rd is not None else np.zeros_like(xd)   # identity: exact
+    pad = nb * 128 - N
+    eyb = np.pad(ey, [(0, 0), (0, 0), (0, pad), (0, 0)]).reshape(B, H, nb, 128 * d).max(axis=-1)
+    amax = s_o * 448.0
+    rel_s = np.where(amax > 0, eyb / np.where(amax > 0, amax, 1.0), 0.0) + 2 * U
+    es = np.abs(s_g - s_o) / s_o
+    log("%s: max rel scale err %.2e (bound %.2e)" % (name, es.max(), rel_s.max()))
+    assert np.all(es <= rel_s), name + ": scales"
+    srep = np.repeat(s_o, 128, axis=-1)[..., :N, None]
+    q_o = np.clip(y_o / srep, -448.0, 448.0)
+    slack = ey / srep + np.abs(q_o) * (np.repeat(rel_s, 128, axis=-1)[..., :N, None] + 3 * U)
+    a = np.abs(q_o)
+    half_step = np.exp2(np.floor(np.log2(np.maximum(a, 2.0 ** -6))) - 3) / 2
+    dec = quant.e4m3_decode(c_g)
+    assert np.all(np.isfinite(dec)), name + ": NaN code"
+    bad = np.abs(dec - q_o) > half_step + slack
+    lo = np.floor(a / (2 * half_step)) * (2 * half_step)
+    unique = np.abs(a - (lo + half_step)) > slack
+    diff = c_g != c_o
+    log("%s: %d of %d codes differ from the oracle's (%d where unique), %d outside the bound"
+        % (name, int(diff.sum()), c_g.size, int((diff & unique).sum()), int(bad.sum())))
+    for i in list(zip(*np.nonzero(diff & unique)))[:6]:
+        log("  differs at %s: y=%.17g s=%.9g q=%.17g gpu=%02x oracle=%02x"
+            % (i, y_o[i], s_o[i[0], i[1], i[2] // 128], q_o[i], c_g[i], c_o[i]))
+    assert not (diff & unique).any(), name + ": codes that are unique differ"
+    assert not bad.any(), name + ": codes"
+
+
+@pytest.mark.parametrize("B,H,N,rot", [(1, 1, 1, True), (1, 2, 300, True), (1, 2, 300, False),
+                                       (2, 3, 128, True), (1, 1, 1000, False), (2, 2, 777, True)])
+def test_quantize_shapes(gpu, B, H, N, rot):
+    x, r = inputs.quant_inputs(B, H, N, 128, seed=1100 + N)
+    log("fa_quantize_fp8 B%d H%d N%d rot=%d" % (B, H, N, rot))
+    codes, scales = fa.fa_quantize_fp8(x.to(gpu), r.to(gpu) if rot else None)
+    torch.cuda.synchronize()
+    check("quant B%dH%dN%d r%d" % (B, H, N, rot), x, r if rot else None, codes, scales)
+
+
+def test_quantize_zero_block_and_reuse(gpu):
+    x, r = inputs.quant_inputs(1, 2, 400, 128, seed=1200)
+    x[:, 1, 128:256] = 0                           # one all-zero block: scale 1, codes 0
+    out_c = torch.full((1, 2, 400, 128), 0x55, dtype=torch.uint8, device=gpu)
+    out_s = torch.full((1, 2, 4), -1.0, dtype=torch.float32, device=gpu)
+    log("fa_quantize_fp8 zero block B1 H2 N400")
+    codes, scales = fa.fa_quantize_fp8(x.to(gpu), r.to(gpu), codes=out_c, scales=out_s)
+    torch.cuda.synchronize()
+    assert codes.data_ptr() == out_c.data_ptr()
+    assert float(scales[0, 1, 1]) == 1.0 and int(codes[0, 1, 128:256].max()) == 0
+    check("quant zero block", x, r, codes, scales)
+
+
+def test_quantize_full_size_B2H16N8192(gpu):
+    """The size and launch the benchmark times: Q and K of the fp8 workload with
+    the rotation, V without, compared in full."""
+    for i, rot in enumerate((True, True, False)):
+        x, r = inputs.quant_inputs(2, 16, 8192, 128, seed=1300 + i)
+        log("fa_quantize_fp8 B2 H16 N8192 d128 rot=%d (full size)" % rot)
+        codes, scales = fa.fa_quantize_fp8(x.to(gpu), r.to(gpu) if rot else None)
+        torch.cuda.synchronize()
+        check("quant full %d" % i, x, r if rot else None, codes, scales)
+
+
+def test_quantize_then_fp8_attention(gpu):
+    """The quantiser's output is fa_fwd_fp8's input: attention on the rotated,
+    quantised Q and K and quantised V matches the oracle on the dequantised
+    values (same bound as the fp8 forward parity), and its distance from exact
+    attention on the unrotated, unquantised bf16 inputs is that of the oracle's
+    own quantise-then-attend pipeline (the rotation cancels in the scores)."""
+    B, H, N, d = 1, 2, 500, 128
+    (q, r), (k, _), (v, _) = [inputs.quant_inputs(B, H, N, d, seed=1400 + i) for i in range(3)]
+    log("fa_quantize_fp8 + fa_fwd_fp8 B1 H2 N500 causal")
+    qc, qs = fa.fa_quantize_fp8(q.to(gpu), r.to(gpu))
+    kc, ks = fa.fa_quantize_fp8(k.to(gpu), r.to(gpu))
+    vc, vs = fa.fa_quantize_fp8(v.to(gpu), None)
+    scale = d ** -0.5
+    o, l = fa.fa_fwd_fp8(qc, kc, vc, qs, ks, vs, scale=scale, causal=True)
+    torch.cuda.synchronize()
+    deq = [quant.dequantize(c.cpu().numpy(), s.cpu().double().numpy()) for c, s in ((qc, qs), (kc, ks), (vc, vs))]
+    ro, rl = oracle.attention(*deq, scale, True)
+    got = f64(o)
+    tol = 8e-2 + np.abs(ro) * 2.0 ** -9
+    assert np.all(np.abs(got - ro) <= tol)
+    assert np.max(np.abs(l.cpu().double().numpy() - rl)) <= 1e-3
+    eo, _ = oracle.attention(f64(q), f64(k), f64(v), scale, True)
+    oq = [quant.rotate_quantize(f64(t), rr) for t, rr in ((q, f64(r)), (k, f64(r)), (v, None))]
+    po, _ = oracle.attention(*[quant.dequantize(c, s) for c, s, _ in oq], scale, True)
+    err = np.linalg.norm(got - eo) / np.linalg.norm(eo)
+    err_o = np.linalg.norm(po - eo) / np.linalg.norm(eo)
+    log("fp8 pipeline vs exact bf16 attention: rel err %.3e (oracle pipeline %.3e)" % (err, err_o))
+    assert err <= err_o + 5e-3
