@@ -162,6 +162,45 @@ constexpr int elem_first(int s) {
     while (e < 32 && elem_slot<S0, W>(e) < s) ++e;
     return e;
 }
+// softmax element E (0..63; keys 32 (E / 32) + E % 32 of group (E % 32) / 16)
+// of a block with NS_PV PV slots and NS_QK QK slots, row max in slots
+// [0, MX]: its fma slot (keys 0..31 before the QK MFMAs rewrite their S
+// registers at slot NS_PV, keys 32..63 in the first half of the QK slots),
+// and its exp slot: an even spread over slots MX + 2 .. NS - 2, never before
+// the slot after its fma. Its sum and pack follow one slot after the exp.
+template <int MX, int NS_PV, int NS_QK>
+constexpr int fma_slot(int E) {
+    return E < 32 ? elem_slot<MX + 1, NS_PV - MX - 1>(E) : elem_slot<NS_PV, NS_QK / 2>(E - 32);
+}
+template <int MX, int NS_PV, int NS_QK>
+constexpr int exp_slot(int E) {
+    const int even = MX + 2 + (E * (NS_PV + NS_QK - MX - 3)) / 64;
+    const int after = fma_slot<MX, NS_PV, NS_QK>(E) + 1;
+    return even > after ? even : after;
+}
+template <int MX, int NS_PV, int NS_QK>
+constexpr int exp_first(int s) {
+    int E = 0;
+    while (E < 64 && exp_slot<MX, NS_PV, NS_QK>(E) < s) ++E;
+    return E;
+}
+// the schedule's order constraints: slots ascend with E; every fma of keys
+// 0..31 precedes slot NS_PV and of keys 32..63 the QK MFMAs of those keys
+// (slot NS_PV + NS_QK / 2); every pack lands inside the block and after the
+// last PV MFMA that reads the P registers it overwrites (pf[g][c] feeds the
+// PV fragments c * DT .. c * DT + DT - 1, slots 2 f and 2 f + 1)
+template <int MX, int NS_PV, int NS_QK, int DT>
+constexpr bool spread_ok() {
+    for (int E = 0; E < 64; ++E) {
+        const int f = fma_slot<MX, NS_PV, NS_QK>(E), x = exp_slot<MX, NS_PV, NS_QK>(E);
+        if (E > 0 && x < exp_slot<MX, NS_PV, NS_QK>(E - 1)) return false;
+        if (f <= MX || x <= f || x + 1 > NS_PV + NS_QK - 1) return false;
+        if (E < 32 ? f >= NS_PV : f >= NS_PV + NS_QK / 2) return false;
+        const int c = 2 * (E / 32) + ((E % 16) >> 3);
+        if (x + 1 <= 2 * (c * DT + DT - 1) + 1) return false;
+    }
+    return true;
+}
 // (this file is built with -fno-honor-nans, so the two maxes become one v_max3)
 __device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
 
@@ -542,39 +581,31 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
                         lsum[gg] *= alpha[gg];
                     }
                 }
-                // keys 0..31: fma (reads S before slot NS_PV overwrites it), exp, sum + pack
+                // fma of keys 0..31 before slot NS_PV (their S registers are
+                // rewritten from there on), of keys 32..63 in the first half of
+                // the QK slots; the exps, sums and packs of all 64 follow one
+                // even spread over the rest of the block
                 constexpr int S1 = MX + 1, W1 = NS_PV - MX - 1;
-                // keys 32..63: fma before the second QK chain, exp and sum spread to the end
                 constexpr int S2 = NS_PV, W2 = NS_QK / 2;
-                constexpr int S3 = NS_PV + 1, W3 = NS - NS_PV - 2;
+                static_assert(spread_ok<MX, NS_PV, NS_QK, DT>(), "softmax slot schedule");
 #pragma unroll
                 for (int e = elem_first<S1, W1>(s); e < elem_first<S1, W1>(s + 1); ++e)
                     x[e / 16][0][e % 16] = fmaf(sacc[e / 16][0][e % 16], ctj[e / 16], -mu[e / 16]);
 #pragma unroll
-                for (int e = elem_first<S1, W1>(s - 1); e < elem_first<S1, W1>(s); ++e)
-                    x[e / 16][0][e % 16] = exp2_hw(x[e / 16][0][e % 16]);
-#pragma unroll
-                for (int e = elem_first<S1, W1>(s - 2); e < elem_first<S1, W1>(s - 1); ++e) {
-                    const int gg = e / 16, i = e % 16;
-                    rsum[gg][0] += x[gg][0][i];
-                    if (i & 1) {
-                        pf[gg][i >> 3][(i & 7) - 1] = (__bf16)x[gg][0][i - 1];
-                        pf[gg][i >> 3][i & 7] = (__bf16)x[gg][0][i];
-                    }
-                }
-#pragma unroll
                 for (int e = elem_first<S2, W2>(s); e < elem_first<S2, W2>(s + 1); ++e)
                     x[e / 16][1][e % 16] = fmaf(sacc[e / 16][1][e % 16], ctj[e / 16], -mu[e / 16]);
+                constexpr int X0 = exp_first<MX, NS_PV, NS_QK>(s - 1), X1 = exp_first<MX, NS_PV, NS_QK>(s),
+                              X2 = exp_first<MX, NS_PV, NS_QK>(s + 1);
 #pragma unroll
-                for (int e = elem_first<S3, W3>(s); e < elem_first<S3, W3>(s + 1); ++e)
-                    x[e / 16][1][e % 16] = exp2_hw(x[e / 16][1][e % 16]);
+                for (int E = X1; E < X2; ++E)
+                    x[(E & 31) / 16][E / 32][E % 16] = exp2_hw(x[(E & 31) / 16][E / 32][E % 16]);
 #pragma unroll
-                for (int e = elem_first<S3, W3>(s - 1); e < elem_first<S3, W3>(s); ++e) {
-                    const int gg = e / 16, i = e % 16;
-                    rsum[gg][1] += x[gg][1][i];
+                for (int E = X0; E < X1; ++E) {
+                    const int gg = (E & 31) / 16, kt = E / 32, i = E % 16;
+                    rsum[gg][kt] += x[gg][kt][i];
                     if (i & 1) {
-                        pf[gg][2 + (i >> 3)][(i & 7) - 1] = (__bf16)x[gg][1][i - 1];
-                        pf[gg][2 + (i >> 3)][i & 7] = (__bf16)x[gg][1][i];
+                        pf[gg][2 * kt + (i >> 3)][(i & 7) - 1] = (__bf16)x[gg][kt][i - 1];
+                        pf[gg][2 * kt + (i >> 3)][i & 7] = (__bf16)x[gg][kt][i];
                     }
                 }
                 if constexpr (s == NS - 1) {
@@ -587,7 +618,7 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
             if constexpr (ISSUE) {
                 static_for<N_ISSUE>([&](auto ic) {
                     constexpr int i = decltype(ic)::value;
-                    if constexpr (2 + i * ((NS - 4) / N_ISSUE) == s) issue_part(j, ic, phc);
+                    if constexpr (NS - 2 * N_ISSUE + 2 * i == s) issue_part(j, ic, phc);
                 });
             }
             __builtin_amdgcn_sched_barrier(0);
