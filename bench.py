@@ -99,9 +99,9 @@ def decode_bytes(p):
 
 def cpu_baseline(x, budget_s=15.0):
     """Time the fp64 oracle on a bounded sample of the causal prefill: query rows
-    i = stride-1 mod stride of the first h heads. A first head at stride 64 sets
-    the pace; the stride and head count are then chosen so that the whole
-    sample takes about budget_s."""
+    i = stride-1 mod stride of the first h heads. A first head at stride 64,
+    timed after one untimed run of it, sets the pace; the stride and head count
+    are then chosen so that the whole sample takes about budget_s."""
     import numpy as np
     import oracle
     B, H, N, d = x.q.shape
@@ -123,6 +123,7 @@ def cpu_baseline(x, budget_s=15.0):
             flops += float(np.sum(4.0 * d * (rows + 1)))
         return flops, t
 
+    run([0])                                 # warm: threads, page faults, caches
     f1, t1 = run([0])
     per_head = max(t1, 1e-3)                 # seconds per head at stride 64
     n_heads = H - 1
@@ -258,8 +259,8 @@ def main():
     ms = {name: sum(a.elapsed_time(b) for a, b in ev[name]) / args.steps for name, _ in parts}
     log("mean ms per launch: %s" % ms)
 
-    def spread(name):
-        t = sorted(a.elapsed_time(b) for a, b in ev[name])
+    def spread(name, launches=1):
+        t = sorted(a.elapsed_time(b) / launches for a, b in ev[name])
         q = lambda f: t[min(len(t) - 1, int(round(f * (len(t) - 1))))]
         return {"p10": q(0.1), "median": q(0.5), "p90": q(0.9)}
     if args.calib_copy_mib:
@@ -348,7 +349,8 @@ def main():
                                         % (int(keep.sum()), nb * (nb + 1) // 2,
                                            ", dropout 0.1" if name.endswith("dropout") else ""),
                             "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS,
-                                         "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS, "traffic": None,
+                                         "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
+                                         "traffic": measured_traffic("pmc_block_sparse_B1H32N16384d128.md"),
                                          "kernel": "sparse_fwd_kernel"}}
     if "fp8_quantize" in ms:
         tokens = 2 * 16 * 8192
@@ -356,7 +358,7 @@ def main():
         per_launch = ms["fp8_quantize"] / 3
         gbs = nbytes / (per_launch * 1e-3) / 1e9
         result["fp8_quantize"] = {"value": 3 * tokens / (ms["fp8_quantize"] * 1e-3), "unit": "tokens/s",
-                                  "launch_ms": per_launch, "launch_ms_spread": spread("fp8_quantize"),
+                                  "launch_ms": per_launch, "launch_ms_spread": spread("fp8_quantize", 3),
                                   "bytes_per_launch": nbytes,
                                   "workload": "rotate + E4M3 block quantise Q, K (Haar R) and V (no R), "
                                               "B2 H16 N8192 d128 each, three launches",
