@@ -22,6 +22,7 @@
 // and the workgroup walks the token blocks grid-stride. A (b, h, block)
 // lives in one workgroup, so its amax needs only an LDS reduction.
 #include "fa_device.h"
+#include "fa_dma.h"
 #include "fa_launch.h"
 #include "fa_tile.h"
 
@@ -69,18 +70,23 @@ __global__ __launch_bounds__(kQzThreads) void fp8_quant_kernel(const uint16_t *_
         __syncthreads();
     }
 
-    for (int item = blockIdx.x; item < total; item += gridDim.x) {
-        const int bh = item / nb, blk = item % nb;
-        const int t0 = blk * kQzBlock;
-        const int my_t = t0 + tl;
-
-        // token my_t, channels 64 h + 8 kc + 0..7 (the MFMA's B operand x^T)
-        u32x4 xb[KC];
-        const uint16_t *xrow = X + ((size_t)bh * N + my_t) * D + 64 * h;
+    // token t0 + tl of an item, channels 64 h + 8 kc + 0..7 (the MFMA's B
+    // operand x^T). Two register sets alternate: the next item's part is
+    // loaded before the current one is processed, so its latency overlaps the
+    // work. The loads always read an in-range address (token 0 of the tensor
+    // for tokens past N or items past the end) and such values are zeroed.
+    auto load_item = [&](int it, u32x4 (&dst)[KC]) __attribute__((always_inline)) {
+        const int my_t = (it % nb) * kQzBlock + tl;
+        const bool in = it < total && my_t < N;
+        const uint16_t *xrow = X + (in ? ((size_t)(it / nb) * N + my_t) * D + 64 * h : (size_t)0);
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc)
-            xb[kc] = my_t < N ? *reinterpret_cast<const u32x4 *>(xrow + 8 * kc) : u32x4{};
-
+        for (int kc = 0; kc < KC; ++kc) {
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(xrow + 8 * kc);
+            dst[kc] = in ? v : u32x4{};
+        }
+    };
+    auto process = [&](int item, const u32x4 (&xb)[KC]) __attribute__((always_inline)) {
+        const int bh = item / nb, t0 = (item % nb) * kQzBlock;
         // ROT: y^T tile nt, lane = token tl, element 4 a + e = output channel
         // 32 nt + 8 a + 4 h + e. Without R, y = x as loaded (signed zeros kept).
         [[maybe_unused]] f32x16 y[NT];
@@ -108,7 +114,7 @@ __global__ __launch_bounds__(kQzThreads) void fp8_quant_kernel(const uint16_t *_
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
         if (lane == 0) wmax[w] = amax;
-        __syncthreads();
+        lds_barrier();   // LDS only: the next item's loads stay in flight
         const float bmax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
         const float s = bmax > 0.f ? bmax / 448.f : 1.f;
         auto code4 = [s](float v0, float v1, float v2, float v3) {
@@ -141,7 +147,7 @@ __global__ __launch_bounds__(kQzThreads) void fp8_quant_kernel(const uint16_t *_
                           code4(bf16_lo(v[2]), bf16_hi(v[2]), bf16_lo(v[3]), bf16_hi(v[3]))};
             }
         }
-        __syncthreads();
+        lds_barrier();
         for (int idx = tid; idx < kQzBlock * D / 16; idx += kQzThreads) {   // 16-byte pieces
             const int r = idx / (D / 16), c = idx % (D / 16);
             if (t0 + r < N)
@@ -149,6 +155,15 @@ __global__ __launch_bounds__(kQzThreads) void fp8_quant_kernel(const uint16_t *_
                     *reinterpret_cast<const u32x4 *>(sc + r * D + 16 * (c ^ ((r >> 1) & 7)));
         }
         if (tid == 0) scales[item] = s;
+    };
+    u32x4 xa[KC], xc[KC];
+    load_item(blockIdx.x, xa);
+    for (int item = blockIdx.x; item < total; item += 2 * (int)gridDim.x) {
+        load_item(item + gridDim.x, xc);
+        process(item, xa);
+        if (item + (int)gridDim.x >= total) break;
+        load_item(item + 2 * gridDim.x, xa);
+        process(item + gridDim.x, xc);
     }
 }
 
