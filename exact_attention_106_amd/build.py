@@ -42,10 +42,14 @@ def common_flags():
 
 # per-source flags: the prefill kernel never produces NaN on purpose (masking
 # uses -inf), and without NaN semantics max(max(a, b), c) is one v_max3
-# backward: MFMA accumulators in VGPRs where they fit (the builtin MFMAs
-# otherwise keep S and dP in AGPRs and copy them out for the softmax)
+# backward and block-sparse forward: MFMA accumulators in VGPRs where they
+# fit (the builtin MFMAs otherwise keep S in AGPRs and copy it out for the
+# softmax, and shuffle O between AGPRs around the rescale branch; measured:
+# the block-sparse forward runs 16 % faster this way, the paged prefill 9 %
+# slower, so that one keeps the default)
 EXTRA = {"fwd_prefill.hip": ["-fno-honor-nans"],
-         "bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+         "bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+         "fwd_sparse.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str) -> str:
