@@ -52,8 +52,9 @@ def prefill_flops(B, H, N, d, causal):
 
 def measured_traffic(summary):
     """HBM bytes per launch from a committed rocprofv3 counter summary
-    (profiles/<summary>), or None when the kernel sources it names have changed
-    since the counters were taken."""
+    (profiles/<summary>), or None when the kernel sources it names (and the
+    build script with their compile flags) have changed since the counters
+    were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", summary)
     if not os.path.exists(path):
