@@ -315,10 +315,13 @@ __device__ __forceinline__ void split_chunk(
 __global__ __launch_bounds__(256) void decode_split_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc,
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ ctx_lens,
-    float *__restrict__ ws, const int *__restrict__ pair, int H, int max_blocks, int max_splits, float c)
+    float *__restrict__ ws, const int *__restrict__ pair, int H, int max_blocks, int max_splits, float c,
+    int head_fastest)
 {
-    const int split = blockIdx.x;
-    const int h = blockIdx.y;
+    // head fastest: the workgroups that run together read the 32 heads' slices
+    // of the same pages, which lie next to each other in the cache
+    const int split = head_fastest ? blockIdx.y : blockIdx.x;
+    const int h = head_fastest ? blockIdx.x : blockIdx.y;
     const int s = blockIdx.z;
     const int n_pages = (ctx_lens[s] + kPS - 1) / kPS;
     if (split * kPPS >= n_pages) return;   // whole workgroup: chunk past the context
@@ -418,9 +421,13 @@ hipError_t launch_paged_decode(const void *q, const void *kcache, const void *vc
                        num_seqs, max_blocks_per_seq, max_splits);
     hipLaunchKernelGGL(decode_pair_kernel, gp, dim3(256), 0, stream, block_table, hash, pair, n_pairs,
                        pair_list, num_seqs, max_blocks_per_seq, max_splits);
-    const dim3 g1((unsigned)max_splits, (unsigned)H, (unsigned)num_seqs);
+    // heads on x where the chunk count fits the y dimension (65535; x has no
+    // such limit), else chunks on x
+    const int head_fastest = max_splits <= 65535 ? 1 : 0;
+    const dim3 g1 = head_fastest ? dim3((unsigned)H, (unsigned)max_splits, (unsigned)num_seqs)
+                                 : dim3((unsigned)max_splits, (unsigned)H, (unsigned)num_seqs);
     hipLaunchKernelGGL(decode_split_kernel, g1, dim3(256), 0, stream, qq, kk, vv, block_table, ctx_lens,
-                       workspace, pair, H, max_blocks_per_seq, max_splits, c);
+                       workspace, pair, H, max_blocks_per_seq, max_splits, c, head_fastest);
     hipLaunchKernelGGL(decode_pair_split_kernel, dim3(kPairGrid), dim3(256), 0, stream, qq, kk, vv,
                        block_table, ctx_lens, workspace, pair, n_pairs, pair_list, H, max_blocks_per_seq,
                        max_splits, c);
