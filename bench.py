@@ -98,7 +98,7 @@ def decode_bytes(p):
     return unique_tok * per_tok + fixed, logical_tok * per_tok + fixed
 
 
-def cpu_baseline(x, budget_s=15.0):
+def cpu_baseline(x, budget_s=20.0):
     """Time the fp64 oracle on a bounded sample of the causal prefill: query rows
     i = stride-1 mod stride of the first h heads. A first head at stride 64,
     timed after one untimed run of it, sets the pace; the stride and head count
@@ -146,7 +146,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--only", default="",
                     help="comma list of prefill,fp8,decode,backward,paged_prefill,block_sparse,"
                          "fp8_quantize (default all)")
