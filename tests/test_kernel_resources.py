@@ -1,0 +1,54 @@
+"""Every gfx950 kernel of the library keeps its working set in registers and
+LDS: no scratch (private memory), no vector-register spills, and LDS within the
+160 KiB of a CU (scalar-register spills go to vector-register lanes, not to
+memory, and are allowed). Scratch in these kernels means register arrays indexed at run time or
+spills, which cost an order of magnitude in speed without changing results, so
+no numerical test would notice. Compiles each HIP source for the device only
+(same flags as the library build) and reads the compiler's resource remarks."""
+import concurrent.futures as cf
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+from exact_attention_106_amd import build as B
+
+LDS_LIMIT = 160 * 1024
+
+
+def remarks(src):
+    with tempfile.TemporaryDirectory() as tmp:
+        cmd = [B.hipcc()] + B.common_flags() + B.EXTRA.get(src, []) + [
+            "--offload-device-only", "-Rpass-analysis=kernel-resource-usage", "-c",
+            os.path.join(B.CSRC, src), "-o", os.path.join(tmp, "k.o")]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    kernels, cur = {}, None
+    for line in r.stderr.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            cur = m.group(1)
+            kernels[cur] = {}
+            continue
+        m = re.search(r"remark:\s+([A-Za-z ]+?)(?: \[bytes/(?:lane|block)\])?: (\d+)", line)
+        if m and cur:
+            kernels[cur][m.group(1).strip()] = int(m.group(2))
+    return kernels
+
+
+@pytest.fixture(scope="module")
+def all_remarks():
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(B.SOURCES))) as ex:
+        return dict(zip(B.SOURCES, ex.map(remarks, B.SOURCES)))
+
+
+@pytest.mark.parametrize("src", [s for s in B.SOURCES if s != "api.hip"])
+def test_no_scratch_no_vgpr_spills(all_remarks, src):
+    kernels = all_remarks[src]
+    assert kernels, "no kernels found in %s" % src
+    for name, k in kernels.items():
+        assert k.get("ScratchSize", 0) == 0, (src, name, k)
+        assert k.get("VGPRs Spill", 0) == 0, (src, name, k)
+        assert k.get("LDS Size", 0) <= LDS_LIMIT, (src, name, k)
