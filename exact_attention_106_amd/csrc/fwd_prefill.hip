@@ -10,8 +10,8 @@
 //   * 4 waves per workgroup, one per SIMD with the whole register file; a
 //     wave owns 64 query rows as two groups of 32 (split-Q), and every K or V
 //     fragment it reads from LDS feeds the MFMAs of both groups;
-//   * K and V tiles of 64 keys stream through LDS rings (3 K tiles, 4 V
-//     tiles) by buffer loads that write LDS directly, two tiles ahead of the
+//   * K and V tiles of 64 keys stream through 4-stage LDS rings (at most 3
+//     K and 4 V tiles live) by buffer loads that write LDS directly, two tiles ahead of the
 //     compute. LDS rows are dense; 16-byte chunks are XOR-swizzled by row so
 //     that both the MFMA operand reads of K and the transpose reads of V are
 //     free of bank conflicts.
@@ -90,7 +90,8 @@ __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w, bool hi) {
 // previous tile is overwritten only slots after its last MFMA read, and the
 // only AGPR writes (rescale) sit between blocks.
 //
-// K has a ring of 3 tiles and V of 4. Block j (or the idle step j of a wave
+// K and V have 4 LDS stages each; at most 3 K tiles (K(j+1) read by the
+// block, K(j+2), K(j+3) in flight) and 4 V tiles are live. Block j (or the idle step j of a wave
 // that is done) issues the copies of V(j+2) and K(j+3); the step before block
 // j waits for V(j) and K(j+1). V(j) is read at the end of block j to prefetch
 // the first fragments of the next block. fp8 V is staged through registers
