@@ -154,7 +154,7 @@ def main():
                     help="after timing, run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the path would shard heads / sequences across GPUs with no communication)",
               file=sys.stderr)
         sys.exit(2)
