@@ -11,7 +11,7 @@
 //   per (b, h, 128-token block): s = fp32(amax|y| / 448) (1 when amax = 0);
 //   code = E4M3FN(round to nearest even of clamp(y / s, -448, 448)), with
 //   the scale as stored, so that decode(code) * s is the E4M3 grid point
-//   nearest to y; y / s is a correctly rounded fp32 division, so an exact tie
+//   nearest to y; y / s is the correctly rounded fp32 quotient, so an exact tie
 //   (possible when no rotation is applied and y = x exactly) goes to the even
 //   code as the definition says.
 // The MFMA computes y^T = R^T x^T, so that a lane ends with 4 consecutive
@@ -117,17 +117,38 @@ __global__ __launch_bounds__(kQzThreads) void fp8_quant_kernel(const uint16_t *_
         lds_barrier();   // LDS only: the next item's loads stay in flight
         const float bmax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
         const float s = bmax > 0.f ? bmax / 448.f : 1.f;
-        auto code4 = [s](float v0, float v1, float v2, float v3) {
-            const float q0 = fminf(fmaxf(v0 / s, -448.f), 448.f), q1 = fminf(fmaxf(v1 / s, -448.f), 448.f);
-            const float q2 = fminf(fmaxf(v2 / s, -448.f), 448.f), q3 = fminf(fmaxf(v3 / s, -448.f), 448.f);
-            const uint32_t lo = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
-            return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, lo, true);
+        // y / s rounded correctly to fp32. For 2^-80 <= s <= 2^100 (every
+        // block of ordinary data) it is refined from q0 = y * RN(1/s) with two
+        // exact-residual steps, e = y - q s by fma and q + e RN(1/s) rounded
+        // (Markstein's quotient refinement: a faithful q and a correctly rounded
+        // reciprocal give the correctly rounded quotient; the first step makes
+        // q faithful). In that range a residual can only fall below the normal
+        // fp32 range when |y / s| < 2^-22, whose code is a signed zero either
+        // way. Outside it, the division instruction sequence.
+        const float r = 1.f / s;
+        const bool refine = s >= 0x1p-80f && s <= 0x1p100f;
+        auto quot = [s, r](float v, auto fc) {
+            if constexpr (decltype(fc)::value) {
+                const float q0 = v * r;
+                const float q1 = __builtin_fmaf(__builtin_fmaf(-q0, s, v), r, q0);
+                const float q = __builtin_fmaf(__builtin_fmaf(-q1, s, v), r, q1);
+                return __builtin_copysignf(q, v);   // -0 stays -0
+            } else {
+                return v / s;
+            }
         };
 
         // codes as rows [token][channel]; the 16-byte chunk c of row r sits at
         // c ^ ((r / 2) % 8), so that the writes of 32 tokens spread over the banks
         uint8_t *srow = sc + tl * D;
         const int sw = (tl >> 1) & 7;
+        auto emit = [&](auto fc) __attribute__((always_inline)) {
+        auto code4 = [&](float v0, float v1, float v2, float v3) {
+            const float q0 = fminf(fmaxf(quot(v0, fc), -448.f), 448.f), q1 = fminf(fmaxf(quot(v1, fc), -448.f), 448.f);
+            const float q2 = fminf(fmaxf(quot(v2, fc), -448.f), 448.f), q3 = fminf(fmaxf(quot(v3, fc), -448.f), 448.f);
+            const uint32_t lo = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
+            return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, lo, true);
+        };
         if constexpr (ROT) {
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
@@ -147,6 +168,9 @@ __global__ __launch_bounds__(kQzThreads) void fp8_quant_kernel(const uint16_t *_
                           code4(bf16_lo(v[2]), bf16_hi(v[2]), bf16_lo(v[3]), bf16_hi(v[3]))};
             }
         }
+        };
+        if (refine) emit(std::true_type{});
+        else emit(std::false_type{});
         lds_barrier();
         for (int idx = tid; idx < kQzBlock * D / 16; idx += kQzThreads) {   // 16-byte pieces
             const int r = idx / (D / 16), c = idx % (D / 16);

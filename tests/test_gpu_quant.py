@@ -72,6 +72,12 @@ def check(name, x, r, codes, scales):
             % (i, y_o[i], s_o[i[0], i[1], i[2] // 128], q_o[i], c_g[i], c_o[i]))
     assert not (diff & unique).any(), name + ": codes that are unique differ"
     assert not bad.any(), name + ": codes"
+    if r is None:
+        # y = x exactly: the scale is the correctly rounded amax / 448 and each
+        # code is decided on the correctly rounded y / s, both as the oracle
+        # does, so scales and codes are bit for bit the oracle's
+        assert np.array_equal(s_g.astype(np.float32), s_o.astype(np.float32)), name + ": exact scales"
+        assert not diff.any(), name + ": exact codes"
 
 
 @pytest.mark.parametrize("B,H,N,rot", [(1, 1, 1, True), (1, 2, 300, True), (1, 2, 300, False),
@@ -95,6 +101,26 @@ def test_quantize_zero_block_and_reuse(gpu):
     assert codes.data_ptr() == out_c.data_ptr()
     assert float(scales[0, 1, 1]) == 1.0 and int(codes[0, 1, 128:256].max()) == 0
     check("quant zero block", x, r, codes, scales)
+
+
+def test_quantize_extreme_block_scales(gpu):
+    """Blocks with scales far below and far above ordinary data (x times 2^-100
+    and 2^110, exact in bf16) next to an ordinary block, with and without R: the
+    kernel divides by the instruction sequence there and refines a multiply by
+    1/s elsewhere; both must give the oracle's scales and codes."""
+    for rot in (False, True):
+        x, r = inputs.quant_inputs(1, 2, 384, 128, seed=1200 + rot)
+        xf = x.float()
+        xf[:, :, :128] *= 2.0 ** -100
+        xf[:, :, 256:] *= 2.0 ** 110
+        xs = xf.to(torch.bfloat16)
+        assert torch.equal(xs.float(), xf), "power-of-two scaling is exact in bf16"
+        log("fa_quantize_fp8 B1 H2 N384 rot=%d, block scales ~2^-106 / 1 / 2^104" % rot)
+        codes, scales = fa.fa_quantize_fp8(xs.to(gpu), r.to(gpu) if rot else None)
+        torch.cuda.synchronize()
+        sc = scales.cpu()
+        assert sc[0, 0, 0] < 2.0 ** -80 and sc[0, 0, 2] > 2.0 ** 100
+        check("quant extreme rot=%d" % rot, xs, r if rot else None, codes, scales)
 
 
 def test_quantize_full_size_B2H16N8192(gpu):
