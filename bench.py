@@ -334,7 +334,7 @@ def main():
                                    "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS,
                                                 "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
                                                 "traffic": measured_traffic("pmc_paged_prefill_S16H32d128.md"),
-                                                "kernel": "paged_prefill_kernel"}}
+                                                "kernel": "fwd_kernel3<128,causal,bf16,paged>"}}
     if "block_sparse" in ms:
         nb = bmask.shape[0]
         keep = bmask.numpy().astype(bool)

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 SOURCES = ["api.hip", "fwd_f32.hip", "fwd_prefill.hip", "decode.hip", "bwd.hip", "block_manager.hip",
-           "paged_prefill.hip", "fwd_sparse.hip", "fp8_quant.hip"]
+           "fwd_sparse.hip", "fp8_quant.hip"]
 ARCH = "gfx950"
 
 

@@ -154,9 +154,9 @@ fa_status fa_paged_prefill(const void *q, const void *kcache, const void *vcache
     if ((long long)num_seqs * H * n_new * d > kMaxElems) return FA_ERR_BAD_SHAPE;
     if ((long long)max_blocks_per_seq * page_size > kMaxElems) return FA_ERR_BAD_SHAPE;
     if (bad_scale(scale)) return FA_ERR_UNSUPPORTED;
-    return from_hip(fa::launch_paged_prefill(q, kcache, vcache, block_table, ctx_lens, o, lse, num_seqs, H,
-                                             n_new, max_blocks_per_seq, scale,
-                                             static_cast<hipStream_t>(stream)));
+    return from_hip(fa::launch_paged_prefill_mfma(q, kcache, vcache, block_table, ctx_lens, o, lse, num_seqs, H,
+                                                  n_new, max_blocks_per_seq, scale,
+                                                  static_cast<hipStream_t>(stream)));
 }
 
 const char *fa_status_str(fa_status s)

@@ -55,10 +55,10 @@ hipError_t launch_fwd_block_sparse(const void *q, const void *k, const void *v, 
                                    void *o, float *lse, int B, int H, int N, float scale, int causal,
                                    float dropout_p, uint64_t seed, hipStream_t stream);
 
-hipError_t launch_paged_prefill(const void *q, const void *kcache, const void *vcache,
-                                const int32_t *block_table, const int32_t *ctx_lens, void *o,
-                                float *lse, int num_seqs, int H, int n_new, int max_blocks_per_seq,
-                                float scale, hipStream_t stream);
+hipError_t launch_paged_prefill_mfma(const void *q, const void *kcache, const void *vcache,
+                                     const int32_t *block_table, const int32_t *ctx_lens, void *o, float *lse,
+                                     int num_seqs, int H, int n_new, int max_blocks_per_seq, float scale,
+                                     hipStream_t stream);
 
 hipError_t launch_paged_decode(const void *q, const void *kcache, const void *vcache,
                                const int32_t *block_table, const int32_t *ctx_lens, void *o,

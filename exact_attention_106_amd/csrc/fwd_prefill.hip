@@ -45,6 +45,16 @@
 // widened E4M3 -> bf16 (exact) on its way into LDS and P.V runs on bf16 MFMA.
 // P is not quantised to E4M3: with V outliers of tens, a 3-bit mantissa on P
 // would exceed this path's accuracy bound.
+//
+// Paged mode (chunked prefill, PagedAttention section of the same page: K/V
+// live in a cache of 16-token pages named by a block table): the same kernel
+// with positions. Query i of sequence s sits at position ctx[s] - N + i and
+// sees keys 0 .. its position; a wave's share of a 64-key tile (rows
+// 16 w .. 16 w + 15) is exactly page 4 t + w, copied with a descriptor that
+// covers the page's valid rows only, so the last page's tail and pages past
+// the context arrive as zeros. Page ids are read one step ahead with scalar
+// loads. With an arbitrary offset between query and key positions a wave may
+// need the mask on two tiles; a query that sees no key gets O = 0, L = -inf.
 #include "fa_device.h"
 #include "fa_dma.h"
 #include "fa_launch.h"
@@ -227,12 +237,25 @@ struct Layout3 {
     static constexpr int MX = NS_PV / 4;     // slots of the row max
 };
 
-template <int D, bool CAUSAL, bool FP8>
+// Paged K/V (chunked prefill through a block table, PagedAttention section of
+// "FlashAttention系列优化"): K and V are caches [pages, H, 16, D]; the N new
+// queries of sequence s sit at positions ctx[s] - N .. ctx[s] - 1 and see
+// cached keys 0 .. their position.
+struct PagedArgs {
+    const int32_t *bt;      // [S, max_blocks] page of each logical block
+    const int32_t *ctx;     // [S] context length (cached tokens, new ones included)
+    uint64_t page_stride;   // bytes from one page to the next (H * 16 * D * 2)
+    int max_blocks;
+    int H;
+};
+
+template <int D, bool CAUSAL, bool FP8, bool PAGED>
 __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
     const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K, const uint8_t *__restrict__ V,
     const float *__restrict__ QS, const float *__restrict__ KSc, const float *__restrict__ VSc,
-    uint16_t *__restrict__ O, float *__restrict__ LSE, int N, int BH, int n_rb, float c0)
+    uint16_t *__restrict__ O, float *__restrict__ LSE, int N, int BH, int n_rb, float c0, PagedArgs pg)
 {
+    static_assert(!PAGED || (CAUSAL && !FP8 && D == 128), "paged: causal bf16, d = 128");
     using L = Layout3<D, FP8>;
     constexpr int KCPR = L::KROW / 16;
     constexpr int VCPR = L::VROW / 16;
@@ -246,8 +269,19 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
     const int l32 = lane & 31;
     const int hf = lane >> 5;
 
-    const int rank = blockIdx.x / BH;
-    const int bh = blockIdx.x % BH;
+    // Workgroup ids go round-robin over the 8 XCDs. Dense: consecutive ids are
+    // the heads of one row block, so all blocks of a head share an XCD. Paged
+    // (many sequence-heads): when B*H is a multiple of 8, all row blocks of one
+    // (sequence, head) get ids of one residue mod 8 and consecutive ids on it,
+    // so they run together on one XCD and read the same pages through its L2
+    int rank = blockIdx.x / BH, bh = blockIdx.x % BH;
+    if constexpr (PAGED) {
+        if (BH % 8 == 0) {
+            const int jx = blockIdx.x / 8;
+            rank = jx % n_rb;
+            bh = 8 * (jx / n_rb) + blockIdx.x % 8;
+        }
+    }
     const int rb = CAUSAL ? (n_rb - 1 - rank) : rank;
     const size_t head_off = (size_t)bh * N * L::KROW;
     const uint32_t head_bytes = (uint32_t)N * L::KROW;
@@ -258,6 +292,29 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
     const int q0 = rb * kBR;
     const int qw = q0 + w * 64;
     const int my_q[2] = {qw + l32, qw + 32 + l32};
+    // keys are positions 0 .. kmax - 1; query i sits at position base_pos + i
+    int kmax = N, base_pos = 0, s_seq = 0, hd = 0;
+    if constexpr (PAGED) {
+        s_seq = bh / pg.H;
+        hd = bh % pg.H;
+        kmax = pg.ctx[s_seq];
+        base_pos = kmax - N;
+        if (base_pos + q0 + kBR <= 0 || kmax <= 0) {
+            // no query of the block sees a key: O = 0, L = -inf
+#pragma unroll
+            for (int g = 0; g < 2; ++g)
+                if (my_q[g] < N) {
+                    uint16_t *orow = O + ((size_t)bh * N + my_q[g]) * D;
+#pragma unroll
+                    for (int t = 0; t < L::DT; ++t)
+#pragma unroll
+                        for (int gg = 0; gg < 4; ++gg)
+                            *reinterpret_cast<u32x2 *>(orow + t * 32 + 8 * gg + 4 * hf) = u32x2{0u, 0u};
+                    if (LSE && hf == 0) LSE[(size_t)bh * N + my_q[g]] = neg_inf();
+                }
+            return;
+        }
+    }
 
     float cg[2] = {c0, c0};
     const float *ks_h = nullptr, *vs_h = nullptr;
@@ -285,14 +342,16 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
                 qa[g][kc] = vload16(rq, (uint32_t)(my_q[g] * D + 16 * kc + 8 * hf) * 2, 0);
         }
 
-    const int kend = CAUSAL ? min(N, q0 + kBR) : N;
+    const int kend = CAUSAL ? min(kmax, base_pos + q0 + kBR) : kmax;
     const int n_tiles = (kend + kBC - 1) / kBC;
+    const int pw = base_pos + qw;   // position of the wave's first query
     // last tile of this wave; for causal the diagonal one (qw is a multiple of
     // 64, so both groups end on it)
-    const int last = CAUSAL ? min(n_tiles - 1, qw / kBC) : n_tiles - 1;
-    // tiles below j_mask are fully visible to the wave's 64 queries; only
-    // `last` can be at or above it
-    const int j_mask = min(CAUSAL ? last : n_tiles, N / kBC);
+    const int last = CAUSAL ? min(n_tiles - 1, pw + kBC - 1 < 0 ? 0 : (pw + kBC - 1) / kBC) : n_tiles - 1;
+    // tiles below j_mask are fully visible to the wave's 64 queries; the
+    // tiles from j_mask to `last` need the mask (one, or two when the queries'
+    // positions are not a multiple of 64 apart from the keys')
+    const int j_mask = CAUSAL ? max(0, (min(pw, kmax - 1) + 1) / kBC) : min(n_tiles, kmax / kBC);
 
     // ---- copies (tiles past the end read zeros into a free stage) ----
     uint32_t kdma_off[L::K_DMA];
@@ -309,20 +368,49 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
         const int r = pos / VCPR, pc = pos % VCPR;
         vdma_off[i] = (uint32_t)(r * L::VROW + ((pc ^ swz<VCPR>(r)) << 4));
     }
+    // paged: the wave's quarter of tile t (rows 16 w .. 16 w + 15) is page 4 t + w;
+    // its descriptor covers the page's valid rows only, so rows past the
+    // context (the last page's tail, pages past the table) read as zeros
+    [[maybe_unused]] uint32_t kpoff[L::K_DMA], vpoff[L::V_DMA > 0 ? L::V_DMA : 1];
+    [[maybe_unused]] const int32_t *bt_s = nullptr;
+    [[maybe_unused]] const uint8_t *kpage0 = nullptr, *vpage0 = nullptr;
+    if constexpr (PAGED) {
+#pragma unroll
+        for (int i = 0; i < L::K_DMA; ++i) kpoff[i] = kdma_off[i] - (uint32_t)w * L::K_DMA * 1024;
+#pragma unroll
+        for (int i = 0; i < L::V_DMA; ++i) vpoff[i] = vdma_off[i] - (uint32_t)w * L::V_DMA * 1024;
+        bt_s = pg.bt + (size_t)s_seq * pg.max_blocks;
+        kpage0 = K + (size_t)hd * (16 * L::KROW);
+        vpage0 = V + (size_t)hd * (16 * L::VROW);
+    }
+    auto valid_rows = [&](int t) { return min(max(kmax - 16 * (4 * t + w), 0), 16); };
+    auto pid_of = [&](int t) -> int { return valid_rows(t) > 0 ? bt_s[4 * t + w] : 0; };
+    auto page_rsrc = [&](const uint8_t *page0, int t, int pid) {
+        return sgpr_rsrc(page0 + (size_t)pid * pg.page_stride, (uint32_t)valid_rows(t) * L::KROW);
+    };
+    [[maybe_unused]] u32x4 pk_cur{}, pv_cur{};   // copies of the current step: K(j+3), V(j+2)
+    [[maybe_unused]] int p2 = 0, p3 = 0;         // pages of tiles j+2, j+3 for the next step
     const uint32_t lds_k = (uint32_t)(size_t)smem;
     const uint32_t lds_v = lds_k + kRing * L::K_TILE;
     // this wave's share of a K / V tile in LDS (stage 0)
     const uint32_t wk_base = __builtin_amdgcn_readfirstlane(lds_k + w * L::K_DMA * 1024);
     const uint32_t wv_base = __builtin_amdgcn_readfirstlane(lds_v + w * L::V_DMA * 1024);
     auto issue_k_part = [&](int j, int i) {
-        dma16(rk, wk_base + (uint32_t)(j & (kRing - 1)) * L::K_TILE + i * 1024, kdma_off[i],
-              (uint32_t)(j * kBC) * L::KROW);
+        if constexpr (PAGED)
+            dma16(page_rsrc(kpage0, j, pid_of(j)), wk_base + (uint32_t)(j & (kRing - 1)) * L::K_TILE + i * 1024,
+                  kpoff[i], 0u);
+        else
+            dma16(rk, wk_base + (uint32_t)(j & (kRing - 1)) * L::K_TILE + i * 1024, kdma_off[i],
+                  (uint32_t)(j * kBC) * L::KROW);
     };
     u32x4 v8reg[L::V8_LOADS > 0 ? L::V8_LOADS : 1];
     auto issue_v_part = [&](int j, int i) {
         const uint32_t soff = (uint32_t)(j * kBC) * L::KROW;
         if constexpr (FP8) {
             v8reg[i] = vload16(rv, (uint32_t)(tid + i * kThreads3) * 16, soff);
+        } else if constexpr (PAGED) {
+            dma16(page_rsrc(vpage0, j, pid_of(j)), wv_base + (uint32_t)(j & (kRing - 1)) * L::V_TILE + i * 1024,
+                  vpoff[i], 0u);
         } else {
             dma16(rv, wv_base + (uint32_t)(j & (kRing - 1)) * L::V_TILE + i * 1024, vdma_off[i], soff);
         }
@@ -334,7 +422,21 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
     auto issue_part = [&](int j, auto ic, auto phc) __attribute__((always_inline)) {
         constexpr int i = decltype(ic)::value;
         constexpr int PH = decltype(phc)::value;
-        if constexpr (PH < 0) {
+        if constexpr (PAGED) {
+            // descriptors of this step's pages, built in the step before the block
+            if constexpr (i < NV_ISSUE) {
+                if constexpr (PH < 0)
+                    dma16(pv_cur, wv_base + (uint32_t)((j + 2) & (kRing - 1)) * L::V_TILE + i * 1024, vpoff[i], 0u);
+                else
+                    dma16c<((PH + 2) & (kRing - 1)) * L::V_TILE + i * 1024>(pv_cur, wv_base, vpoff[i], 0u);
+            } else {
+                constexpr int ik = i - NV_ISSUE;
+                if constexpr (PH < 0)
+                    dma16(pk_cur, wk_base + (uint32_t)((j + 3) & (kRing - 1)) * L::K_TILE + ik * 1024, kpoff[ik], 0u);
+                else
+                    dma16c<((PH + 3) & (kRing - 1)) * L::K_TILE + ik * 1024>(pk_cur, wk_base, kpoff[ik], 0u);
+            }
+        } else if constexpr (PH < 0) {
             if constexpr (i < NV_ISSUE) issue_v_part(FP8 ? j + 1 : j + 2, i);
             else issue_k_part(j + 3, i - NV_ISSUE);
         } else if constexpr (i < NV_ISSUE) {
@@ -501,7 +603,7 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
             const int k0 = j * kBC;
 #pragma unroll
             for (int g = 0; g < 2; ++g) {
-                const int lim = (CAUSAL ? min(qw + 32 * g + l32, N - 1) : N - 1) - (k0 + 4 * hf);
+                const int lim = (CAUSAL ? min(base_pos + qw + 32 * g + l32, kmax - 1) : kmax - 1) - (k0 + 4 * hf);
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -688,6 +790,12 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
             wait_vm(L::V_DMA + L::K_DMA);
         }
         lds_barrier();
+        if constexpr (PAGED) {
+            pv_cur = page_rsrc(vpage0, j + 2, p2);
+            pk_cur = page_rsrc(kpage0, j + 3, p3);
+            p2 = p3;
+            p3 = pid_of(j + 4);   // first used in the next step, after its barrier
+        }
     };
 
     // ---- prologue ----
@@ -712,6 +820,10 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
         for (int i = 0; i < L::V_DMA; ++i) issue_v_part(1, i);
 #pragma unroll
         for (int i = 0; i < L::K_DMA; ++i) issue_k_part(2, i);
+        if constexpr (PAGED) {
+            p2 = pid_of(2);
+            p3 = pid_of(3);
+        }
         wait_vm(2 * L::K_DMA + 2 * L::V_DMA);     // Q and K(0)
     }
     // the loads are asm: pin their results after the wait (a copy placed
@@ -734,19 +846,21 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
     if (last >= 1) block(0, 0 >= j_mask, F{}, T{}, T{}, T{}, T{}, G{});
     else block(0, true, F{}, F{}, T{}, T{}, T{}, G{});
     // ---- blocks 1 .. last-1 ----
-    auto step = [&](int j, auto phc) __attribute__((always_inline)) {
+    auto step = [&](int j, auto phc, bool masked) __attribute__((always_inline)) {
         rescale();
         mid(j);
-        block(j, false, T{}, T{}, T{}, T{}, T{}, phc);
+        block(j, masked, T{}, T{}, T{}, T{}, T{}, phc);
     };
     int j = 1;
-    for (; j + 3 < last; j += 4) {   // unrolled over the 4 LDS stages (j & 3 == 1, 2, 3, 0)
-        step(j, std::integral_constant<int, 1>{});
-        step(j + 1, std::integral_constant<int, 2>{});
-        step(j + 2, std::integral_constant<int, 3>{});
-        step(j + 3, std::integral_constant<int, 0>{});
+    // blocks below j_open need no mask (dense: only `last` can need one)
+    const int j_open = PAGED ? min(last, j_mask) : last;
+    for (; j + 3 < j_open; j += 4) {   // unrolled over the 4 LDS stages (j & 3 == 1, 2, 3, 0)
+        step(j, std::integral_constant<int, 1>{}, false);
+        step(j + 1, std::integral_constant<int, 2>{}, false);
+        step(j + 2, std::integral_constant<int, 3>{}, false);
+        step(j + 3, std::integral_constant<int, 0>{}, false);
     }
-    for (; j < last; ++j) step(j, G{});
+    for (; j < last; ++j) step(j, G{}, PAGED && j >= j_mask);
     // ---- block last ----
     if (last >= 1) {
         rescale();
@@ -775,7 +889,7 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
     for (int g = 0; g < 2; ++g) {
         const float lt = other_half_sum(lsum[g]);
         if (my_q[g] < N) {
-            const float inv = 1.f / lt;
+            const float inv = lt > 0.f ? 1.f / lt : 0.f;   // a query with no visible key: O = 0
             uint16_t *orow = O + ((size_t)bh * N + my_q[g]) * D;
 #pragma unroll
             for (int t = 0; t < DT; ++t)
@@ -799,10 +913,10 @@ hipError_t launch_t(const void *q, const void *k, const void *v, const float *qs
     const int n_rb = (N + kBR - 1) / kBR;
     const int BH = B * H;
     const dim3 grid((unsigned)((size_t)BH * n_rb));
-    hipLaunchKernelGGL((fwd_kernel3<D, CAUSAL, FP8>), grid, dim3(kThreads3), 0, stream,
+    hipLaunchKernelGGL((fwd_kernel3<D, CAUSAL, FP8, false>), grid, dim3(kThreads3), 0, stream,
                        static_cast<const uint8_t *>(q), static_cast<const uint8_t *>(k),
                        static_cast<const uint8_t *>(v), qs, ks, vs, static_cast<uint16_t *>(o), lse, N,
-                       BH, n_rb, scale * kLog2e);
+                       BH, n_rb, scale * kLog2e, PagedArgs{});
     return hipGetLastError();
 }
 
@@ -816,6 +930,24 @@ hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, void *o,
                       : launch_t<64, false, false>(q, k, v, nullptr, nullptr, nullptr, o, lse, B, H, N, scale, stream);
     return causal ? launch_t<128, true, false>(q, k, v, nullptr, nullptr, nullptr, o, lse, B, H, N, scale, stream)
                   : launch_t<128, false, false>(q, k, v, nullptr, nullptr, nullptr, o, lse, B, H, N, scale, stream);
+}
+
+// chunked prefill through the block table: the n_new newest tokens of each
+// sequence (q [S, H, n_new, 128]) against its paged cache [pages, H, 16, 128]
+hipError_t launch_paged_prefill_mfma(const void *q, const void *kcache, const void *vcache,
+                                     const int32_t *block_table, const int32_t *ctx_lens, void *o, float *lse,
+                                     int num_seqs, int H, int n_new, int max_blocks_per_seq, float scale,
+                                     hipStream_t stream)
+{
+    const int n_rb = (n_new + kBR - 1) / kBR;
+    const int BH = num_seqs * H;
+    const dim3 grid((unsigned)((size_t)BH * n_rb));
+    const PagedArgs pg{block_table, ctx_lens, (uint64_t)H * 16 * 128 * 2, max_blocks_per_seq, H};
+    hipLaunchKernelGGL((fwd_kernel3<128, true, false, true>), grid, dim3(kThreads3), 0, stream,
+                       static_cast<const uint8_t *>(q), static_cast<const uint8_t *>(kcache),
+                       static_cast<const uint8_t *>(vcache), nullptr, nullptr, nullptr, static_cast<uint16_t *>(o),
+                       lse, n_new, BH, n_rb, scale * kLog2e, pg);
+    return hipGetLastError();
 }
 
 hipError_t launch_fwd_fp8(const uint8_t *q8, const uint8_t *k8, const uint8_t *v8, const float *qs,
