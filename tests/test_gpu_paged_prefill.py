@@ -53,6 +53,24 @@ def test_paged_prefill_pools(gpu, n_new, ctx_lo, ctx_hi):
     check("paged prefill n_new=%d" % n_new, o, l, ro, rl)
 
 
+@pytest.mark.parametrize("S,H,n_new,ctx_lo,ctx_hi", [
+    (3, 3, 300, 100, 900),    # S*H not a multiple of 8 (plain workgroup order), ragged row block
+    (5, 1, 600, 500, 1300),   # three row blocks, contexts not multiples of 64
+    (2, 4, 520, 512, 1024),   # XCD-grouped order, a row block of 8 queries
+    (2, 2, 700, 100, 400)])   # row blocks entirely before the context (O = 0, L = -inf)
+def test_paged_prefill_grids(gpu, S, H, n_new, ctx_lo, ctx_hi):
+    p = inputs.paged_pool(num_seqs=S, H=H, d=128, ctx_lo=ctx_lo, ctx_hi=ctx_hi, seed=60 + n_new)
+    q = inputs.dense(S, H, n_new, 128, seed=61 + n_new).q
+    log("fa_paged_prefill S%d H%d n_new=%d ctx=%s" % (S, H, n_new, p.ctx_lens.tolist()))
+    o, l = fa.fa_paged_prefill(q.to(gpu), p.kcache.to(gpu), p.vcache.to(gpu), p.block_table.to(gpu),
+                               p.ctx_lens.to(gpu), scale=p.scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.paged_prefill(f64(q), bits(p.kcache), bits(p.vcache), p.block_table.numpy(),
+                                  p.ctx_lens.numpy(), p.scale)
+    check("paged prefill S%d H%d n_new=%d" % (S, H, n_new), o, l, ro, rl)
+    assert np.array_equal(np.isneginf(l.cpu().numpy()), np.isneginf(rl)), "queries that see no key"
+
+
 def test_block_manager_fork_cow_prefill(gpu):
     """Prompt of 100 tokens, forked into three samples that each add 20 tokens:
     shared prompt pages, one copy-on-write per sample on the half-full last
