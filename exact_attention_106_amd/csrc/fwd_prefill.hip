@@ -181,18 +181,35 @@ constexpr int elem_first(int s) {
 // the slot after its fma. Its sum and pack follow one slot after the exp.
 template <int MX, int NS_PV, int NS_QK>
 constexpr int fma_slot(int E) {
+    if (NS_QK < NS_PV)   // fp8: short QK chains, every fma in the PV slots
+        return MX + 1 + (E * (NS_PV - MX - 1)) / 64;
     return E < 32 ? elem_slot<MX + 1, NS_PV - MX - 1>(E) : elem_slot<NS_PV, NS_QK / 2>(E - 32);
 }
 template <int MX, int NS_PV, int NS_QK>
 constexpr int exp_slot(int E) {
-    const int even = MX + 2 + (E * (NS_PV + NS_QK - MX - 3)) / 64;
+    // fp8: a QK slot lasts two PV slots; spread in time
+    const int WQ = NS_QK < NS_PV ? 2 : 1;
+    const int u0 = MX + 2, u1 = NS_PV + (NS_QK - 2) * WQ;
+    const int u = u0 + (E * (u1 - u0 + 1)) / 64;
+    const int even = u < NS_PV ? u : NS_PV + (u - NS_PV) / WQ;
     const int after = fma_slot<MX, NS_PV, NS_QK>(E) + 1;
-    return even > after ? even : after;
+    // the pack one slot later must follow the last PV MFMA reading the P
+    // registers it overwrites (pf[g][c] feeds slots up to 2 (c DT + DT - 1) + 1)
+    const int DT = NS_PV / 8, c = 2 * (E / 32) + ((E % 16) >> 3);
+    const int need = 2 * (c * DT + DT - 1) + 1;
+    const int m1 = even > after ? even : after;
+    return m1 > need ? m1 : need;
 }
 template <int MX, int NS_PV, int NS_QK>
 constexpr int exp_first(int s) {
     int E = 0;
     while (E < 64 && exp_slot<MX, NS_PV, NS_QK>(E) < s) ++E;
+    return E;
+}
+template <int MX, int NS_PV, int NS_QK>
+constexpr int fma_first(int s) {
+    int E = 0;
+    while (E < 64 && fma_slot<MX, NS_PV, NS_QK>(E) < s) ++E;
     return E;
 }
 // the schedule's order constraints: slots ascend with E; every fma of keys
@@ -691,12 +708,20 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
                 constexpr int S1 = MX + 1, W1 = NS_PV - MX - 1;
                 constexpr int S2 = NS_PV, W2 = NS_QK / 2;
                 static_assert(spread_ok<MX, NS_PV, NS_QK, DT>(), "softmax slot schedule");
+                if constexpr (NS_QK < NS_PV) {
+                    constexpr int F0 = fma_first<MX, NS_PV, NS_QK>(s), F1 = fma_first<MX, NS_PV, NS_QK>(s + 1);
 #pragma unroll
-                for (int e = elem_first<S1, W1>(s); e < elem_first<S1, W1>(s + 1); ++e)
-                    x[e / 16][0][e % 16] = fmaf(sacc[e / 16][0][e % 16], ctj[e / 16], -mu[e / 16]);
+                    for (int E = F0; E < F1; ++E)
+                        x[(E & 31) / 16][E / 32][E % 16] =
+                            fmaf(sacc[(E & 31) / 16][E / 32][E % 16], ctj[(E & 31) / 16], -mu[(E & 31) / 16]);
+                } else {
 #pragma unroll
-                for (int e = elem_first<S2, W2>(s); e < elem_first<S2, W2>(s + 1); ++e)
-                    x[e / 16][1][e % 16] = fmaf(sacc[e / 16][1][e % 16], ctj[e / 16], -mu[e / 16]);
+                    for (int e = elem_first<S1, W1>(s); e < elem_first<S1, W1>(s + 1); ++e)
+                        x[e / 16][0][e % 16] = fmaf(sacc[e / 16][0][e % 16], ctj[e / 16], -mu[e / 16]);
+#pragma unroll
+                    for (int e = elem_first<S2, W2>(s); e < elem_first<S2, W2>(s + 1); ++e)
+                        x[e / 16][1][e % 16] = fmaf(sacc[e / 16][1][e % 16], ctj[e / 16], -mu[e / 16]);
+                }
                 constexpr int X0 = exp_first<MX, NS_PV, NS_QK>(s - 1), X1 = exp_first<MX, NS_PV, NS_QK>(s),
                               X2 = exp_first<MX, NS_PV, NS_QK>(s + 1);
 #pragma unroll
