@@ -10,6 +10,7 @@ first call does, and raises if it has not been built.
 from __future__ import annotations
 
 import ctypes
+import functools
 import math
 from typing import Optional, Tuple
 
@@ -30,6 +31,24 @@ def _ptr(t: Optional[torch.Tensor]):
 
 def _stream(t: torch.Tensor):
     return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _on_device(fn):
+    """Run an entry point under the device of its tensors: the library launches
+    on the current HIP device with the caller's stream of that device, so all
+    tensor arguments must share one device, which is made current for the call."""
+    @functools.wraps(fn)
+    def wrapper(*args, **kwargs):
+        devs = {a.device for a in list(args) + list(kwargs.values())
+                if isinstance(a, torch.Tensor) and a.device.type == "cuda"}
+        if len(devs) > 1:
+            raise ValueError("%s: all tensors must be on one device, got %s"
+                             % (fn.__name__, sorted(str(d) for d in devs)))
+        if not devs:
+            return fn(*args, **kwargs)
+        with torch.cuda.device(devs.pop()):
+            return fn(*args, **kwargs)
+    return wrapper
 
 
 def _check_dev(name, t, dtype, shape=None):
@@ -62,6 +81,7 @@ def _dense_common(q, k, v, dtype, out, lse, out_dtype):
     return B, H, N, d, out
 
 
+@_on_device
 def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float] = None,
            causal: bool = False, out: Optional[torch.Tensor] = None,
            lse: Optional[torch.Tensor] = None, return_lse: bool = True
@@ -78,6 +98,7 @@ def fa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[fl
     return out, lse
 
 
+@_on_device
 def fa_fwd_f32(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float] = None,
                causal: bool = False, out: Optional[torch.Tensor] = None,
                lse: Optional[torch.Tensor] = None, return_lse: bool = True
@@ -100,6 +121,7 @@ def _as_u8(name, t):
     return t
 
 
+@_on_device
 def fa_fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, q_scale: torch.Tensor,
                k_scale: torch.Tensor, v_scale: torch.Tensor, scale: Optional[float] = None,
                causal: bool = False, out: Optional[torch.Tensor] = None,
@@ -131,6 +153,7 @@ def fa_fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, q_scale: to
     return out, lse
 
 
+@_on_device
 def fa_quantize_fp8(x: torch.Tensor, rot: Optional[torch.Tensor] = None,
                     codes: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None
                     ) -> Tuple[torch.Tensor, torch.Tensor]:
@@ -158,6 +181,7 @@ def fa_quantize_fp8(x: torch.Tensor, rot: Optional[torch.Tensor] = None,
     return codes, scales
 
 
+@_on_device
 def fa_fwd_block_sparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: torch.Tensor,
                         scale: Optional[float] = None, causal: bool = False, dropout_p: float = 0.0,
                         seed: int = 0, out: Optional[torch.Tensor] = None,
@@ -184,6 +208,7 @@ def fa_bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
     return int(_lib.load().fa_bwd_workspace_bytes(B, H, N, d))
 
 
+@_on_device
 def fa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
            dout: torch.Tensor, scale: Optional[float] = None, causal: bool = False,
            workspace: Optional[torch.Tensor] = None, dq: Optional[torch.Tensor] = None,
@@ -219,6 +244,7 @@ def fa_paged_decode_workspace_bytes(num_seqs: int, H: int, d: int, page_size: in
                                                            max_blocks_per_seq))
 
 
+@_on_device
 def fa_paged_decode(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
                     block_table: torch.Tensor, ctx_lens: torch.Tensor,
                     scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
@@ -260,6 +286,7 @@ def fa_paged_decode(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
     return out, lse
 
 
+@_on_device
 def fa_paged_prefill(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
                      block_table: torch.Tensor, ctx_lens: torch.Tensor, scale: Optional[float] = None,
                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
@@ -343,6 +370,7 @@ class BlockManager:
         return table, ctx
 
 
+@_on_device
 def fa_copy_pages(kcache: torch.Tensor, vcache: torch.Tensor, src: torch.Tensor, dst: torch.Tensor) -> None:
     """Copy pages src[i] -> dst[i] of both caches (bf16 [P, H, page_size, d]); src, dst device int32 [n]."""
     _check_dev("kcache", kcache, torch.bfloat16)
