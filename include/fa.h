@@ -13,7 +13,9 @@
  *   - Pointers are DEVICE pointers (HBM) unless stated otherwise; the caller
  *     owns every buffer. The library allocates nothing and never synchronises:
  *     all work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
- *     the default stream), so results are ready once the stream is.
+ *     the default stream), so results are ready once the stream is. Kernels
+ *     launch on the calling thread's current HIP device: the buffers and the
+ *     stream must belong to it.
  *   - Tensors are dense row-major: q/k/v/o [B, H, N, d], lse [B, H, N] fp32.
  *   - Natural logarithms; L is in the units of the scaled scores.
  *   - causal != 0: key j is visible to query i iff j <= i (top-left aligned,
