@@ -215,3 +215,45 @@ def paged_prefill(q, kcache_bits, vcache_bits, block_table, ctx_lens, scale: flo
                                                   scale, True)
     return o, lse
 
+
+
+def attention_bwd_rows(q, k, v, dout, rows, scale: float, causal: bool):
+    """dq at query rows `rows` of one head (q, k, v, dout [n, d]): the same
+    chain rule as ``attention_bwd``, row by row. Row i needs only its own
+    weights: p_i = softmax(s_i), dp_ij = dO_i . v_j, D_i = sum_j p_ij dp_ij,
+    ds_ij = p_ij (dp_ij - D_i), dq_i = scale sum_j ds_ij k_j. Returns fp64 [R, d]."""
+    q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(dout)
+    rows = np.asarray(rows, dtype=np.int64).reshape(-1)
+    n = k.shape[0]
+    s = scale * (q[rows] @ k.T)
+    if causal:
+        s = np.where(np.arange(n)[None, :] <= rows[:, None], s, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    p = e / e.sum(axis=1, keepdims=True)
+    dp = g[rows] @ v.T
+    dd = np.sum(p * dp, axis=1, keepdims=True)
+    ds = p * (dp - dd)
+    return scale * (ds @ k)
+
+
+def attention_bwd_cols(q, k, v, dout, cols, scale: float, causal: bool):
+    """dk and dv at key rows `cols` of one head (q, k, v, dout [n, d]): sums over
+    the queries that see key j of the same chain-rule terms,
+      dv_j = sum_i p_ij dO_i,  dk_j = scale sum_i p_ij (dp_ij - D_i) q_i,
+    with p_ij = exp(s_ij - L_i) from the row logsumexp L_i and D_i =
+    sum_j p_ij dp_ij = dO_i . O_i (O_i = sum_j p_ij v_j), both taken from this
+    oracle's forward pass over all rows. Returns (dk [C, d], dv [C, d]) fp64."""
+    q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(dout)
+    cols = np.asarray(cols, dtype=np.int64).reshape(-1)
+    n = q.shape[0]
+    o, lse = attention(q[None, None], k[None, None], v[None, None], scale, causal)
+    o, lse = o[0, 0], lse[0, 0]
+    dd = np.sum(g * o, axis=1)
+    s = scale * (q @ k[cols].T)                       # [n, C]
+    if causal:
+        s = np.where(np.arange(n)[:, None] >= cols[None, :], s, -np.inf)
+    p = np.exp(s - lse[:, None])
+    dp = g @ v[cols].T
+    ds = p * (dp - dd[:, None])
+    return scale * (ds.T @ q), p.T @ g

@@ -16,7 +16,8 @@ What it computes, per (batch, head), written out from the definitions:
 The keep decision uses Philox4x32-10 as published by Salmon, Moraes, Dror and
 Shaw ("Parallel random numbers: as easy as 1, 2, 3", SC 2011): key (seed low,
 seed high 32 bits), counter (j // 4, i, b * H + h, 0); z_ij = 0 iff word j % 4
-of the output is below floor(p_drop * 2^32).
+of the output is below floor(p_drop * 2^32), p_drop taken as the float32
+value the C interface receives.
 """
 from __future__ import annotations
 
@@ -42,16 +43,34 @@ def philox4x32_10(c0, c1, c2, c3, k0: int, k1: int):
     return [x.astype(np.uint32) for x in c]
 
 
-def keep_mask(n: int, bh: int, p_drop: float, seed: int) -> np.ndarray:
-    """z [n, n] (bool) of one head: True where the weight is kept."""
-    thr = int(p_drop * 4294967296.0)
+def _as_f32(p: float) -> float:
+    return float(np.float32(p))
+
+
+def drop_threshold(p_drop: float) -> int:
+    """floor(p * 2^32) for the probability as the library receives it: the
+    dropout_p argument of the C interface is a 32-bit float, so p is first
+    rounded to float32 (0.1 gives 429496736, not 429496729)."""
+    return int(_as_f32(p_drop) * 4294967296.0)
+
+
+def keep_rows(rows, n: int, bh: int, p_drop: float, seed: int) -> np.ndarray:
+    """z [len(rows), n] (bool): keep decisions of query rows `rows` against
+    keys 0..n-1 of head bh; True where the weight is kept."""
+    rows = np.asarray(rows, dtype=np.uint64).reshape(-1)
+    thr = drop_threshold(p_drop)
     if thr == 0:
-        return np.ones((n, n), dtype=bool)
-    i = np.arange(n, dtype=np.uint64)[:, None]
+        return np.ones((rows.size, n), dtype=bool)
+    i = rows[:, None]
     j4 = np.arange((n + 3) // 4, dtype=np.uint64)[None, :]
     words = philox4x32_10(j4, i, np.uint64(bh), np.uint64(0), seed & 0xFFFFFFFF, seed >> 32)
-    u = np.stack(words, axis=-1).reshape(n, -1)[:, :n]      # u[i, j] = word j % 4 of counter j // 4
+    u = np.stack(words, axis=-1).reshape(rows.size, -1)[:, :n]   # u[r, j] = word j % 4 of counter j // 4
     return u >= np.uint32(thr)
+
+
+def keep_mask(n: int, bh: int, p_drop: float, seed: int) -> np.ndarray:
+    """z [n, n] (bool) of one head: True where the weight is kept."""
+    return keep_rows(np.arange(n), n, bh, p_drop, seed)
 
 
 def block_sparse_attention(q, k, v, block_mask, scale: float, causal: bool, p_drop: float = 0.0,
@@ -78,6 +97,36 @@ def block_sparse_attention(q, k, v, block_mask, scale: float, causal: bool, p_dr
             p = np.zeros_like(s)
             p[rows] = e[rows] / l[rows, None]
             z = keep_mask(N, b * H + h, p_drop, seed)
-            o[b, h] = (p * z / (1.0 - p_drop)) @ v[b, h]
+            o[b, h] = (p * z / (1.0 - _as_f32(p_drop))) @ v[b, h]
             lse[b, h, rows] = m[rows] + np.log(l[rows])
+    return o, lse
+
+
+def block_sparse_attention_rows(q_rows, rows, k, v, block_mask, scale: float, causal: bool, bh: int,
+                                p_drop: float = 0.0, seed: int = 0, block: int = 128):
+    """The same definition for selected query rows of one head.
+
+    q_rows [R, d] are the queries at positions `rows`; k, v [N, d]; bh = b * H
+    + h names the head in the dropout counter. Returns (o [R, d], lse [R]) fp64.
+    """
+    q_rows, k, v = (np.asarray(x, dtype=np.float64) for x in (q_rows, k, v))
+    rows = np.asarray(rows, dtype=np.int64).reshape(-1)
+    bm = np.asarray(block_mask) != 0
+    n = k.shape[0]
+    j = np.arange(n)
+    vis = bm[rows[:, None] // block, j[None, :] // block]
+    if causal:
+        vis &= j[None, :] <= rows[:, None]
+    s = np.where(vis, scale * (q_rows @ k.T), -np.inf)
+    m = s.max(axis=1)
+    live = np.isfinite(m)
+    e = np.zeros_like(s)
+    e[live] = np.exp(s[live] - m[live, None])
+    l = e.sum(axis=1)
+    p = np.zeros_like(s)
+    p[live] = e[live] / l[live, None]
+    z = keep_rows(rows, n, bh, p_drop, seed)
+    o = (p * z / (1.0 - _as_f32(p_drop))) @ v
+    lse = np.full(rows.size, -np.inf)
+    lse[live] = m[live] + np.log(l[live])
     return o, lse

@@ -85,3 +85,18 @@ def test_bwd_closed_forms():
     assert np.max(np.abs(dk)) < 1e-15
     vc = v[0] - v[0].mean(axis=0)
     np.testing.assert_allclose(dq[0], 0.8 / n * (g[0] @ vc.T) @ k[0], atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_row_and_column_samplers_match_full_backward(causal):
+    # the samplers used at full size against the full chain-rule oracle
+    rng = np.random.default_rng(31 + causal)
+    n, d = 203, 16
+    q, k, v, g = (rng.standard_normal((n, d)) for _ in range(4))
+    dq, dk, dv = oracle.attention_bwd(q[None], k[None], v[None], g[None], 0.3, causal)
+    idx = np.array([0, 1, 2, 63, 64, 127, 128, 150, 201, 202])
+    np.testing.assert_allclose(oracle.attention_bwd_rows(q, k, v, g, idx, 0.3, causal), dq[0][idx],
+                               rtol=0, atol=1e-12)
+    sk, sv = oracle.attention_bwd_cols(q, k, v, g, idx, 0.3, causal)
+    np.testing.assert_allclose(sk, dk[0][idx], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(sv, dv[0][idx], rtol=0, atol=1e-12)
