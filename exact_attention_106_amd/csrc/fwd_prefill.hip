@@ -273,6 +273,7 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
     uint16_t *__restrict__ O, float *__restrict__ LSE, int N, int BH, int n_rb, float c0, PagedArgs pg)
 {
     static_assert(!PAGED || (CAUSAL && !FP8 && D == 128), "paged: causal bf16, d = 128");
+    static_assert(!FP8 || D == 128, "fp8: d = 128 (the V chunk map covers 64 rows x 8 chunks with 2 loads per lane)");
     using L = Layout3<D, FP8>;
     constexpr int KCPR = L::KROW / 16;
     constexpr int VCPR = L::VROW / 16;
@@ -338,8 +339,10 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
     if constexpr (FP8) {
         const int nsb = (N + kScaleBlock - 1) / kScaleBlock;
         const float *qs_h = QS + (size_t)bh * nsb;
-        cg[0] = c0 * qs_h[min(qw / kScaleBlock, nsb - 1)];
-        cg[1] = c0 * qs_h[min((qw + 32) / kScaleBlock, nsb - 1)];
+        // Q and K scales below 2^-100 (zero included) act as 2^-100, so that
+        // the multiplier stays positive and masked -inf scores stay -inf
+        cg[0] = c0 * fmaxf(qs_h[min(qw / kScaleBlock, nsb - 1)], 0x1p-100f);
+        cg[1] = c0 * fmaxf(qs_h[min((qw + 32) / kScaleBlock, nsb - 1)], 0x1p-100f);
         ks_h = KSc + (size_t)bh * nsb;
         vs_h = VSc + (size_t)bh * nsb;
     }
@@ -420,11 +423,22 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
             dma16(rk, wk_base + (uint32_t)(j & (kRing - 1)) * L::K_TILE + i * 1024, kdma_off[i],
                   (uint32_t)(j * kBC) * L::KROW);
     };
+    // fp8 V: 16-byte chunk idx = tid + 256 i of a tile is row v8_row(idx),
+    // chunk v8_chunk(idx) (16 E4M3 values). The 16 lanes of one LDS write pass
+    // then hold 16 consecutive rows at one chunk, which the row swizzle spreads
+    // over all banks (a row-major assignment puts 8 lanes of a pass on the even
+    // chunks of one row and 8 on those of the next: two-way conflicts)
+    auto v8_row = [](int idx) { return (idx & 15) + 16 * (idx >> 7); };
+    auto v8_chunk = [](int idx) { return (idx >> 4) & 7; };
+    auto v8_goff = [&](int i) {
+        const int idx = tid + i * kThreads3;
+        return (uint32_t)(v8_row(idx) * D + 16 * v8_chunk(idx));
+    };
     u32x4 v8reg[L::V8_LOADS > 0 ? L::V8_LOADS : 1];
     auto issue_v_part = [&](int j, int i) {
         const uint32_t soff = (uint32_t)(j * kBC) * L::KROW;
         if constexpr (FP8) {
-            v8reg[i] = vload16(rv, (uint32_t)(tid + i * kThreads3) * 16, soff);
+            v8reg[i] = vload16(rv, v8_goff(i), soff);
         } else if constexpr (PAGED) {
             dma16(page_rsrc(vpage0, j, pid_of(j)), wv_base + (uint32_t)(j & (kRing - 1)) * L::V_TILE + i * 1024,
                   vpoff[i], 0u);
@@ -459,7 +473,7 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
         } else if constexpr (i < NV_ISSUE) {
             const uint32_t soff = (uint32_t)((FP8 ? j + 1 : j + 2) * kBC) * L::KROW;
             if constexpr (FP8)
-                v8reg[i] = vload16(rv, (uint32_t)(tid + i * kThreads3) * 16, soff);
+                v8reg[i] = vload16(rv, v8_goff(i), soff);
             else
                 dma16c<((PH + 2) & (kRing - 1)) * L::V_TILE + i * 1024>(rv, wv_base, vdma_off[i], soff);
         } else {
@@ -474,7 +488,7 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
         for (int i = 0; i < L::V8_LOADS; ++i) {
             asm volatile("" : "+v"(v8reg[i]));
             const int idx = tid + i * kThreads3;
-            const int r = idx / (D / 16), c8 = idx % (D / 16);
+            const int r = v8_row(idx), c8 = v8_chunk(idx);
             u32x4 lo, hi;
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
@@ -693,7 +707,9 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
                         const float mxc = other_half_max(mx[gg]) * ctj[gg];
                         const bool move = mxc > m[gg] + kRescaleSlack;
                         const float m_new = move ? mxc : m[gg];
-                        alpha[gg] = exp2_hw(m[gg] - m_new);
+                        // a row that has seen no key yet keeps m = -inf, and
+                        // 2^(-inf - -inf) would be NaN: alpha is 1 unless m moves
+                        alpha[gg] = move ? exp2_hw(m[gg] - m_new) : 1.f;
                         moved[gg] = __builtin_amdgcn_ballot_w64(move) != 0;
                         m[gg] = m_new;
                         mu[gg] = m_new == neg_inf() ? 0.f : m_new;
@@ -802,8 +818,9 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
         if constexpr (FP8) {
             wait_vm(j == 0 ? 0 : L::K_DMA);
             store_v8(j);
-            ctj[0] = cg[0] * ks_h[min(j, n_tiles - 1) * kBC / kScaleBlock];
-            ctj[1] = cg[1] * ks_h[min(j, n_tiles - 1) * kBC / kScaleBlock];
+            const float ksj = fmaxf(ks_h[min(j, n_tiles - 1) * kBC / kScaleBlock], 0x1p-100f);
+            ctj[0] = cg[0] * ksj;
+            ctj[1] = cg[1] * ksj;
             // P of the tile is computed as vs * exp2(t): log2 vs joins the
             // exponent's bias and l gets the sum back in units of exp2(t).
             // Scales below 2^-100 (zero included) act as 2^-100: such a
@@ -925,7 +942,7 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
                     packed[1] = pack_bf16x2(oacc[g][t][4 * gg + 2] * inv, oacc[g][t][4 * gg + 3] * inv);
                     *reinterpret_cast<u32x2 *>(orow + t * 32 + 8 * gg + 4 * hf) = packed;
                 }
-            if (LSE && hf == 0) LSE[(size_t)bh * N + my_q[g]] = (m[g] + __log2f(lt)) * kLn2;
+            if (LSE && hf == 0) LSE[(size_t)bh * N + my_q[g]] = lt > 0.f ? (m[g] + __log2f(lt)) * kLn2 : neg_inf();
         }
     }
 }

@@ -53,6 +53,9 @@ typedef enum fa_status {
  * q, k, v: bf16 [B, H, N, d]; o: bf16 [B, H, N, d] (rounded to nearest even);
  * lse: fp32 [B, H, N] (may be NULL to skip it).
  * d in {64, 128}; B, H, N >= 1 with B*H*N*d < 2^31.
+ * q, k and v must be finite (the kernel is built without NaN and infinity
+ * semantics; a NaN or infinite input leaves O and L undefined), and the
+ * weighted sums must stay in fp32 range: |v| < 2^64.
  * Tiling (row blocks of Q in parallel, K/V tiles streamed through on-chip
  * memory, online softmax with one final 1/l): "FlashAttention系列优化",
  * FlashAttentionV2 section and its equations.
@@ -74,9 +77,11 @@ fa_status fa_fwd_f32(const float *q, const float *k, const float *v, float *o, f
  * q8, k8, v8: OCP E4M3FN bytes [B, H, N, d]; q_scale, k_scale, v_scale: fp32
  * [B, H, ceil(N/128)], one per (batch, head, 128-token block); the value of an
  * element is decode(x8) * scale of its block. o: bf16 [B, H, N, d];
- * lse: fp32 [B, H, N] or NULL. d == 128. Scales are finite; v_scale entries
- * are >= 0, and one below 2^-100 (zero included) acts as 2^-100. Q.K^T runs
- * on fp8 MFMA; P.V runs on bf16 MFMA with V widened exactly from E4M3 to bf16.
+ * lse: fp32 [B, H, N] or NULL. d == 128. Codes are finite (no 0x7f / 0xff)
+ * and scales finite and >= 0; a q_scale, k_scale or v_scale entry below
+ * 2^-100 (zero included) acts as 2^-100, which keeps the score multiplier
+ * positive and moves O by far less than a bf16 ulp. Q.K^T runs on fp8 MFMA;
+ * P.V runs on bf16 MFMA with V widened exactly from E4M3 to bf16.
  */
 fa_status fa_fwd_fp8(const uint8_t *q8, const uint8_t *k8, const uint8_t *v8,
                      const float *q_scale, const float *k_scale, const float *v_scale,
