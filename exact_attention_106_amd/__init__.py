@@ -20,7 +20,8 @@ from . import _lib
 from ._lib import FaError
 
 __all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_quantize_fp8", "fa_fwd_block_sparse", "fa_bwd", "fa_bwd_workspace_bytes",
-           "fa_paged_decode", "fa_paged_decode_workspace_bytes", "fa_paged_prefill", "BlockManager",
+           "fa_paged_decode", "fa_paged_decode_workspace_bytes", "fa_paged_decode_noalloc",
+           "fa_noalloc_scratch_bytes", "fa_paged_prefill", "BlockManager",
            "fa_copy_pages",
            "fa_status_str", "fa_version", "FaError"]
 
@@ -284,6 +285,41 @@ def fa_paged_decode(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
                                      workspace.numel(), _stream(q))
     _lib.check(st, "fa_paged_decode")
     return out, lse
+
+
+def fa_noalloc_scratch_bytes() -> int:
+    return int(_lib.load().fa_noalloc_scratch_bytes())
+
+
+@_on_device
+def fa_paged_decode_noalloc(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
+                            block_table: torch.Tensor, ctx_lens: torch.Tensor, out: torch.Tensor,
+                            lse: Optional[torch.Tensor] = None, scale: Optional[float] = None) -> None:
+    """fa_paged_decode with the library's static workspace: allocates nothing
+    (no workspace, no outputs), so the caller passes `out` (and `lse`, or None).
+    Same shapes as fa_paged_decode; raises FaError(FA_ERR_SCRATCH_LIMIT) when the
+    sizes need more than fa_noalloc_scratch_bytes() of workspace."""
+    _check_dev("q", q, torch.bfloat16)
+    if q.dim() != 3:
+        raise ValueError("q must be [S, H, d]")
+    S, H, d = q.shape
+    _check_dev("kcache", kcache, torch.bfloat16)
+    if kcache.dim() != 4 or kcache.shape[1] != H or kcache.shape[3] != d:
+        raise ValueError("kcache must be [P, H, page_size, d]")
+    _check_dev("vcache", vcache, torch.bfloat16, kcache.shape)
+    P, _, page_size, _ = kcache.shape
+    _check_dev("block_table", block_table, torch.int32)
+    if block_table.dim() != 2 or block_table.shape[0] != S:
+        raise ValueError("block_table must be [S, max_blocks]")
+    _check_dev("ctx_lens", ctx_lens, torch.int32, (S,))
+    _check_dev("out", out, torch.bfloat16, (S, H, d))
+    if lse is not None:
+        _check_dev("lse", lse, torch.float32, (S, H))
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = _lib.load().fa_paged_decode_noalloc(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(block_table),
+                                             _ptr(ctx_lens), _ptr(out), _ptr(lse), S, H, d, page_size,
+                                             block_table.shape[1], P, scale, _stream(q))
+    _lib.check(st, "fa_paged_decode_noalloc")
 
 
 @_on_device

@@ -12,10 +12,12 @@ FA_OK = 0
 STATUS_NAMES = {
     0: "FA_OK", 1: "FA_ERR_NULL_PTR", 2: "FA_ERR_BAD_SHAPE", 3: "FA_ERR_UNSUPPORTED",
     4: "FA_ERR_WORKSPACE", 5: "FA_ERR_HIP", 6: "FA_ERR_NO_PAGES", 7: "FA_ERR_STATE",
+    8: "FA_ERR_SCRATCH_LIMIT",
 }
 # every symbol include/fa.h declares
 EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_quantize_fp8", "fa_fwd_block_sparse", "fa_bwd_workspace_bytes", "fa_bwd",
-           "fa_paged_decode_workspace_bytes", "fa_paged_decode", "fa_paged_prefill",
+           "fa_paged_decode_workspace_bytes", "fa_paged_decode", "fa_noalloc_scratch_bytes",
+           "fa_paged_decode_noalloc", "fa_paged_prefill",
            "fa_bm_state_bytes", "fa_bm_init",
            "fa_bm_add_seq", "fa_bm_fork", "fa_bm_append_token", "fa_bm_free_seq",
            "fa_bm_num_free_pages", "fa_bm_seq_len", "fa_bm_page_refcount", "fa_bm_block_table",
@@ -56,6 +58,10 @@ def load() -> ctypes.CDLL:
         lib.fa_paged_decode_workspace_bytes.restype = sz
         lib.fa_paged_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
         lib.fa_paged_decode.restype = i
+        lib.fa_noalloc_scratch_bytes.argtypes = []
+        lib.fa_noalloc_scratch_bytes.restype = sz
+        lib.fa_paged_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+        lib.fa_paged_decode_noalloc.restype = i
         lib.fa_quantize_fp8.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
         lib.fa_quantize_fp8.restype = i
         lib.fa_fwd_block_sparse.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, f, ctypes.c_uint64, vp]

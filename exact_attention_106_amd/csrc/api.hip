@@ -116,14 +116,12 @@ size_t fa_paged_decode_workspace_bytes(int num_seqs, int H, int d, int page_size
     return fa::decode_workspace_bytes(num_seqs, H, max_blocks_per_seq);
 }
 
-fa_status fa_paged_decode(const void *q, const void *kcache, const void *vcache,
-                          const int32_t *block_table, const int32_t *ctx_lens, void *o, float *lse,
-                          int num_seqs, int H, int d, int page_size, int max_blocks_per_seq,
-                          int num_pages, float scale, void *workspace, size_t workspace_bytes,
-                          void *stream)
+static fa_status check_paged_decode(const void *q, const void *kcache, const void *vcache,
+                                    const int32_t *block_table, const int32_t *ctx_lens, const void *o,
+                                    int num_seqs, int H, int d, int page_size, int max_blocks_per_seq,
+                                    int num_pages, float scale)
 {
-    if (!q || !kcache || !vcache || !block_table || !ctx_lens || !o || !workspace)
-        return FA_ERR_NULL_PTR;
+    if (!q || !kcache || !vcache || !block_table || !ctx_lens || !o) return FA_ERR_NULL_PTR;
     if (num_seqs <= 0 || H <= 0 || d <= 0 || page_size <= 0 || max_blocks_per_seq <= 0 ||
         num_pages <= 0)
         return FA_ERR_BAD_SHAPE;
@@ -131,6 +129,19 @@ fa_status fa_paged_decode(const void *q, const void *kcache, const void *vcache,
     if (num_seqs > 65535 || H > 65535) return FA_ERR_BAD_SHAPE;
     if ((long long)max_blocks_per_seq * page_size > kMaxElems) return FA_ERR_BAD_SHAPE;
     if (bad_scale(scale)) return FA_ERR_UNSUPPORTED;
+    return FA_OK;
+}
+
+fa_status fa_paged_decode(const void *q, const void *kcache, const void *vcache,
+                          const int32_t *block_table, const int32_t *ctx_lens, void *o, float *lse,
+                          int num_seqs, int H, int d, int page_size, int max_blocks_per_seq,
+                          int num_pages, float scale, void *workspace, size_t workspace_bytes,
+                          void *stream)
+{
+    fa_status st = check_paged_decode(q, kcache, vcache, block_table, ctx_lens, o, num_seqs, H, d, page_size,
+                                      max_blocks_per_seq, num_pages, scale);
+    if (st != FA_OK) return st;
+    if (!workspace) return FA_ERR_NULL_PTR;
     if (workspace_bytes < fa_paged_decode_workspace_bytes(num_seqs, H, d, page_size,
                                                           max_blocks_per_seq))
         return FA_ERR_WORKSPACE;
@@ -138,6 +149,23 @@ fa_status fa_paged_decode(const void *q, const void *kcache, const void *vcache,
                                             num_seqs, H, d, page_size, max_blocks_per_seq, scale,
                                             static_cast<float *>(workspace),
                                             static_cast<hipStream_t>(stream)));
+}
+
+size_t fa_noalloc_scratch_bytes(void) { return fa::kNoallocScratchBytes; }
+
+fa_status fa_paged_decode_noalloc(const void *q, const void *kcache, const void *vcache,
+                                  const int32_t *block_table, const int32_t *ctx_lens, void *o, float *lse,
+                                  int num_seqs, int H, int d, int page_size, int max_blocks_per_seq,
+                                  int num_pages, float scale, void *stream)
+{
+    fa_status st = check_paged_decode(q, kcache, vcache, block_table, ctx_lens, o, num_seqs, H, d, page_size,
+                                      max_blocks_per_seq, num_pages, scale);
+    if (st != FA_OK) return st;
+    if (fa_paged_decode_workspace_bytes(num_seqs, H, d, page_size, max_blocks_per_seq) > fa::kNoallocScratchBytes)
+        return FA_ERR_SCRATCH_LIMIT;
+    return from_hip(fa::launch_paged_decode_noalloc(q, kcache, vcache, block_table, ctx_lens, o, lse, num_seqs,
+                                                    H, d, page_size, max_blocks_per_seq, scale,
+                                                    static_cast<hipStream_t>(stream)));
 }
 
 fa_status fa_paged_prefill(const void *q, const void *kcache, const void *vcache,
@@ -170,6 +198,8 @@ const char *fa_status_str(fa_status s)
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported an error";
     case FA_ERR_NO_PAGES: return "FA_ERR_NO_PAGES: the block manager has no free page";
     case FA_ERR_STATE: return "FA_ERR_STATE: invalid block-manager state or sequence id in the wrong state";
+    case FA_ERR_SCRATCH_LIMIT:
+        return "FA_ERR_SCRATCH_LIMIT: the sizes need more workspace than the library's static buffer holds";
     }
     return "unknown fa_status";
 }

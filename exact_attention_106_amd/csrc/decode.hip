@@ -28,6 +28,8 @@
 #include "fa_device.h"
 #include "fa_launch.h"
 
+#include <mutex>
+
 namespace fa {
 namespace {
 
@@ -437,6 +439,56 @@ hipError_t launch_paged_decode(const void *q, const void *kcache, const void *vc
     hipLaunchKernelGGL(decode_merge_kernel, g2, dim3(kMergeThreads), 0, stream, workspace, ctx_lens,
                        static_cast<uint16_t *>(o), lse, H, max_splits);
     return hipGetLastError();
+}
+
+// ---- the same decode with a static workspace (no allocation anywhere) ----
+// For callers that cannot allocate device memory. Each device holds its own
+// copy of this buffer from the time the library's code is loaded on it until
+// the process ends. Host code never passes `scratch` itself to a kernel (on
+// the host that name is only a stand-in): its device address is looked up
+// once per device with hipGetSymbolAddress and kept in scratch_ptr.
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_ptr[kMaxDevices] = {};
+
+// device address of `scratch` on the current device (looked up on its first use)
+hipError_t scratch_address(void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_paged_decode_noalloc(const void *q, const void *kcache, const void *vcache,
+                                       const int32_t *block_table, const int32_t *ctx_lens, void *o,
+                                       float *lse, int num_seqs, int H, int d, int page_size,
+                                       int max_blocks_per_seq, float scale, hipStream_t stream)
+{
+    if (decode_workspace_bytes(num_seqs, H, max_blocks_per_seq) > kNoallocScratchBytes)
+        return hipErrorInvalidValue;   // the C ABI rejects such sizes before this
+    void *ws = nullptr;
+    const hipError_t e = scratch_address(&ws);
+    if (e != hipSuccess) return e;
+    // every word of the workspace the kernels read is written earlier in the
+    // same call (partials, hashes, pair slots; the pair count is reset by the
+    // first kernel), so the buffer needs no clearing between calls
+    return launch_paged_decode(q, kcache, vcache, block_table, ctx_lens, o, lse, num_seqs, H, d, page_size,
+                               max_blocks_per_seq, scale, static_cast<float *>(ws), stream);
 }
 
 }  // namespace fa

@@ -66,4 +66,15 @@ hipError_t launch_paged_decode(const void *q, const void *kcache, const void *vc
                                int max_blocks_per_seq, float scale, float *workspace,
                                hipStream_t stream);
 
+// Size of the static device buffer that serves as the paged decode's
+// workspace in the entry point that allocates nothing (one per device).
+constexpr size_t kNoallocScratchBytes = (size_t)80 << 20;
+
+// The paged decode on the current device with its workspace in that static
+// buffer. The caller has checked decode_workspace_bytes(...) <= kNoallocScratchBytes.
+hipError_t launch_paged_decode_noalloc(const void *q, const void *kcache, const void *vcache,
+                                       const int32_t *block_table, const int32_t *ctx_lens, void *o,
+                                       float *lse, int num_seqs, int H, int d, int page_size,
+                                       int max_blocks_per_seq, float scale, hipStream_t stream);
+
 }  // namespace fa

@@ -44,8 +44,10 @@ typedef enum fa_status {
     FA_ERR_WORKSPACE = 4,    /* workspace too small */
     FA_ERR_HIP = 5,          /* the HIP runtime reported an error at launch */
     FA_ERR_NO_PAGES = 6,     /* block manager: no free page left */
-    FA_ERR_STATE = 7         /* block manager: invalid state, or the sequence is
+    FA_ERR_STATE = 7,        /* block manager: invalid state, or the sequence is
                                 absent / already present */
+    FA_ERR_SCRATCH_LIMIT = 8 /* the call needs more workspace than the library's
+                                static buffer holds (fa_paged_decode_noalloc) */
 } fa_status;
 
 /*
@@ -195,6 +197,32 @@ fa_status fa_paged_decode(const void *q, const void *kcache, const void *vcache,
                           int page_size, int max_blocks_per_seq, int num_pages,
                           float scale, void *workspace, size_t workspace_bytes,
                           void *stream);
+
+/*
+ * fa_paged_decode for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same operation, arguments, kernels and results as fa_paged_decode, but the
+ * workspace is a static device buffer inside the library
+ * (fa_noalloc_scratch_bytes() = 80 MiB per device, held from the time the
+ * library's code is loaded on a device until the process ends). No call
+ * allocates or frees memory.
+ * Sizes whose fa_paged_decode_workspace_bytes(...) exceeds that buffer return
+ * FA_ERR_SCRATCH_LIMIT before anything is launched. That bound is about
+ * num_seqs * H * ceil(max_blocks_per_seq / 32) <= 161000 (for example 64
+ * sequences x 32 heads with max_blocks_per_seq up to 2496, i.e. contexts up to
+ * 39936 tokens).
+ * Every call on one device shares that device's buffer: calls that can overlap
+ * on one device (different streams, or several host threads) race and must be
+ * ordered by the caller; calls on one stream are ordered by the stream. The
+ * buffer keeps the last call's contents; each call writes every part of it
+ * that it reads, so nothing needs clearing.
+ */
+size_t fa_noalloc_scratch_bytes(void);
+fa_status fa_paged_decode_noalloc(const void *q, const void *kcache, const void *vcache,
+                                  const int32_t *block_table, const int32_t *ctx_lens,
+                                  void *o, float *lse, int num_seqs, int H, int d,
+                                  int page_size, int max_blocks_per_seq, int num_pages,
+                                  float scale, void *stream);
 
 /*
  * Paged (chunked) prefill: the n_new newest tokens of each sequence attend to

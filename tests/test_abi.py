@@ -148,3 +148,23 @@ def test_quantize_validation(lib):
     assert call(x=FAKE + 8) == UNSUPPORTED          # 16-byte alignment
     assert call(r=FAKE + 2) == UNSUPPORTED
     assert call(s=FAKE + 2) == UNSUPPORTED
+
+
+def test_paged_decode_noalloc_validation(lib):
+    # the static workspace bounds the sizes: 80 MiB per device
+    limit = lib.fa_noalloc_scratch_bytes()
+    assert limit == 80 << 20
+    assert lib.fa_paged_decode_workspace_bytes(64, 32, 128, 16, 2496) <= limit
+    assert lib.fa_paged_decode_workspace_bytes(64, 32, 128, 16, 2497) > limit
+
+    def call(d=128, ps=16, S=64, mb=2048, P=100, q=FAKE, o=FAKE, scale=0.1):
+        return lib.fa_paged_decode_noalloc(q, FAKE, FAKE, FAKE, FAKE, o, None, S, 32, d, ps, mb, P, scale, None)
+    assert call(q=None) == NULL_PTR
+    assert call(o=None) == NULL_PTR
+    assert call(S=0) == BAD_SHAPE
+    assert call(P=0) == BAD_SHAPE
+    assert call(d=64) == UNSUPPORTED
+    assert call(ps=32) == UNSUPPORTED
+    assert call(scale=0.0) == UNSUPPORTED
+    assert call(mb=2497) == 8                       # FA_ERR_SCRATCH_LIMIT, before any launch
+    assert call(S=65536) == BAD_SHAPE
