@@ -105,7 +105,8 @@ __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w, bool hi) {
 // that is done) issues the copies of V(j+2) and K(j+3); the step before block
 // j waits for V(j) and K(j+1). V(j) is read at the end of block j to prefetch
 // the first fragments of the next block. fp8 V is staged through registers
-// (loaded in block j-1, converted to bf16 and stored before block j).
+// (loaded at the start of block j-1, converted to bf16 and stored before
+// block j).
 constexpr int kThreads3 = 256;
 constexpr int kRing = 4;    // LDS stages of K and of V
 
@@ -758,11 +759,16 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
                         lsum[gg] += FP8 ? (rsum[gg][0] + rsum[gg][1]) * ipsj : rsum[gg][0] + rsum[gg][1];
                 }
             }
-            // 5. copies of this step, spread over the block
+            // 5. copies of this step: tile copies in the last slots, which
+            // carry the least VALU work; fp8 V register loads in the first
+            // slots, so that they have the whole block to arrive before the
+            // step that stores them (issued late they left only a few slots,
+            // and the wait before the next block stalled on memory latency)
             if constexpr (ISSUE) {
                 static_for<N_ISSUE>([&](auto ic) {
                     constexpr int i = decltype(ic)::value;
-                    if constexpr (NS - 2 * N_ISSUE + 2 * i == s) issue_part(j, ic, phc);
+                    constexpr int slot = (FP8 && i < NV_ISSUE) ? 2 * i : NS - 2 * N_ISSUE + 2 * i;
+                    if constexpr (slot == s) issue_part(j, ic, phc);
                 });
             }
             __builtin_amdgcn_sched_barrier(0);
