@@ -483,24 +483,26 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
                                                                      (uint32_t)((j + 3) * kBC) * L::KROW);
         }
     };
-    auto store_v8 = [&](int j) __attribute__((always_inline)) {
+    // widen the i-th register load of V(j) to bf16 and store it in V(j)'s stage
+    auto store_v8_part = [&](int j, int i) __attribute__((always_inline)) {
         uint8_t *sv = smem + kRing * L::K_TILE + (j & (kRing - 1)) * L::V_TILE;
+        asm volatile("" : "+v"(v8reg[i]));
+        const int idx = tid + i * kThreads3;
+        const int r = v8_row(idx), c8 = v8_chunk(idx);
+        u32x4 lo, hi;
 #pragma unroll
-        for (int i = 0; i < L::V8_LOADS; ++i) {
-            asm volatile("" : "+v"(v8reg[i]));
-            const int idx = tid + i * kThreads3;
-            const int r = v8_row(idx), c8 = v8_chunk(idx);
-            u32x4 lo, hi;
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                lo[2 * e] = e4m3x2_to_bf16x2(v8reg[i][e], false);
-                lo[2 * e + 1] = e4m3x2_to_bf16x2(v8reg[i][e], true);
-                hi[2 * e] = e4m3x2_to_bf16x2(v8reg[i][2 + e], false);
-                hi[2 * e + 1] = e4m3x2_to_bf16x2(v8reg[i][2 + e], true);
-            }
-            *reinterpret_cast<u32x4 *>(sv + r * L::VROW + (((2 * c8) ^ swz<VCPR>(r)) << 4)) = lo;
-            *reinterpret_cast<u32x4 *>(sv + r * L::VROW + (((2 * c8 + 1) ^ swz<VCPR>(r)) << 4)) = hi;
+        for (int e = 0; e < 2; ++e) {
+            lo[2 * e] = e4m3x2_to_bf16x2(v8reg[i][e], false);
+            lo[2 * e + 1] = e4m3x2_to_bf16x2(v8reg[i][e], true);
+            hi[2 * e] = e4m3x2_to_bf16x2(v8reg[i][2 + e], false);
+            hi[2 * e + 1] = e4m3x2_to_bf16x2(v8reg[i][2 + e], true);
         }
+        *reinterpret_cast<u32x4 *>(sv + r * L::VROW + (((2 * c8) ^ swz<VCPR>(r)) << 4)) = lo;
+        *reinterpret_cast<u32x4 *>(sv + r * L::VROW + (((2 * c8 + 1) ^ swz<VCPR>(r)) << 4)) = hi;
+    };
+    auto store_v8 = [&](int j) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < L::V8_LOADS; ++i) store_v8_part(j, i);
     };
 
     // ---- operand-read offsets of this lane ----
@@ -759,6 +761,19 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
                         lsum[gg] += FP8 ? (rsum[gg][0] + rsum[gg][1]) * ipsj : rsum[gg][0] + rsum[gg][1];
                 }
             }
+            // fp8: V(j+1), loaded at the start of this block, is widened and
+            // stored into its stage in the first QK slots (that stage held
+            // V(j-3), whose last reads every wave finished before the barrier
+            // of this step). Only this block's V loads and older copies are
+            // outstanding there (its K copies come later), so the wait is
+            // for all of them; the next step's barrier publishes the stores.
+            if constexpr (FP8 && ISSUE) {
+                if constexpr (s == NS_PV) {
+                    wait_vm_n<0>();
+                    store_v8_part(j + 1, 0);
+                }
+                if constexpr (s == NS_PV + 2) store_v8_part(j + 1, 1);
+            }
             // 5. copies of this step: tile copies in the last slots, which
             // carry the least VALU work; fp8 V register loads in the first
             // slots, so that they have the whole block to arrive before the
@@ -819,25 +834,33 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
                 asm volatile("s_nop 4");
             }
     };
-    // the step before block j: V(j) and K(j+1) in (fp8: V(j) stored), barrier
+    // the step before block j: V(j) and K(j+1) in (fp8: V(0) stored here,
+    // later tiles by the block before), barrier
+    [[maybe_unused]] float ks_nx = 0.f, vs_nx = 0.f;   // fp8: K and V scales of the next tile
     auto mid = [&](int j) __attribute__((always_inline)) {
         if constexpr (FP8) {
             wait_vm(j == 0 ? 0 : L::K_DMA);
-            store_v8(j);
-            const float ksj = fmaxf(ks_h[min(j, n_tiles - 1) * kBC / kScaleBlock], 0x1p-100f);
+            if (j == 0) store_v8(0);
+            const float ksj = fmaxf(ks_nx, 0x1p-100f);
             ctj[0] = cg[0] * ksj;
             ctj[1] = cg[1] * ksj;
             // P of the tile is computed as vs * exp2(t): log2 vs joins the
             // exponent's bias and l gets the sum back in units of exp2(t).
             // Scales below 2^-100 (zero included) act as 2^-100: such a
             // block's V is 0 to far below bf16 resolution.
-            lps = __builtin_amdgcn_logf(fmaxf(vs_h[min(j, n_tiles - 1) * kBC / kScaleBlock], 0x1p-100f));
+            lps = __builtin_amdgcn_logf(fmaxf(vs_nx, 0x1p-100f));
             ipsj = exp2_hw(-lps);
             asm volatile("" : "+v"(ctj[0]), "+v"(ctj[1]), "+v"(lps), "+v"(ipsj));
         } else {
             wait_vm(L::V_DMA + L::K_DMA);
         }
         lds_barrier();
+        if constexpr (FP8) {
+            // the next tile's scales, loaded a step ahead (the barrier above
+            // waits on every scalar load, so one issued before it would stall it)
+            ks_nx = ks_h[min(j + 1, n_tiles - 1) * kBC / kScaleBlock];
+            vs_nx = vs_h[min(j + 1, n_tiles - 1) * kBC / kScaleBlock];
+        }
         if constexpr (PAGED) {
             pv_cur = page_rsrc(vpage0, j + 2, p2);
             pk_cur = page_rsrc(kpage0, j + 3, p3);
@@ -847,6 +870,10 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
     };
 
     // ---- prologue ----
+    if constexpr (FP8) {
+        ks_nx = ks_h[0];
+        vs_nx = vs_h[0];
+    }
     for (int i = tid; i < L::LDS / 16; i += kThreads3) reinterpret_cast<u32x4 *>(smem)[i] = u32x4{};
     lds_barrier();
     if constexpr (FP8) {
@@ -924,10 +951,14 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
     for (int jj = last + 1; jj < n_tiles; ++jj) {
         mid(jj);
         static_for<N_ISSUE>([&](auto ic) { issue_part(jj, ic, G{}); });
+        if constexpr (FP8) {   // what the block of this step would store: V(jj+1)
+            wait_vm(L::K_DMA);
+            store_v8(jj + 1);
+        }
     }
     wait_vm(0);
-    // fp8: the last register loads of V are never stored; keeping them live
-    // up to the wait stops their registers from being reused while in flight
+    // fp8: keeping the last register loads of V live up to the wait stops
+    // their registers from being reused while in flight
 #pragma unroll
     for (int i = 0; i < L::V8_LOADS; ++i) asm volatile("" : "+v"(v8reg[i]));
     asm volatile("s_nop 15\n\ts_nop 15");
