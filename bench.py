@@ -12,11 +12,16 @@ One step = one pass of the whole path over resident synthetic inputs:
   6. fa_fwd_block_sparse  the inputs of (1) with a seeded block mask keeping
                  half of the causal 128 x 128 blocks (the diagonal always),
                  without and with dropout p = 0.1
+  7. fa_quantize_fp8  rotation + E4M3 block quantiser of the fp8 workload's
+                 Q, K (with R) and V (without)
+  8. fa_fwd      bf16 non-causal MHA, B=4 H=16 N=2048 d=64
 Each launch is bracketed by HIP events on the stream it runs on. `value` is
 the prefill's TFLOP/s (4*B*H*N^2*d, halved for causal, per the kernel's mean
 event time); decode GB/s and fp8 TFLOP/s are reported beside it. The CPU
-baseline is the fp64 oracle, timed on a bounded sample of the prefill
-workload on this host's cores.
+baselines are the fp64 oracle, timed on bounded samples of the prefill and
+decode workloads on this host's cores. After the timed steps the headline
+prefill runs back to back for about a second while the GPU's gfx clock is
+sampled (amdsmi), for a clock-adjusted fraction of peak beside the spec one.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
@@ -140,6 +145,143 @@ def cpu_baseline(x, budget_s=20.0):
                                                             n_heads * len(rows), f, t)}
 
 
+def device_info(dev):
+    """GPU name, ROCm / HIP versions and host CPU of this run."""
+    import torch
+    info = {"gpu": torch.cuda.get_device_name(dev),
+            "arch": torch.cuda.get_device_properties(dev).gcnArchName,
+            "compute_units": torch.cuda.get_device_properties(dev).multi_processor_count,
+            "hip": torch.version.hip}
+    try:
+        info["rocm"] = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        info["rocm"] = None
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        try:
+            h = amdsmi.amdsmi_get_processor_handles()[0]
+            info["market_name"] = amdsmi.amdsmi_get_gpu_asic_info(h).get("market_name")
+            try:
+                info["product_name"] = amdsmi.amdsmi_get_gpu_board_info(h).get("product_name")
+            except Exception:
+                info["product_name"] = None
+        finally:
+            amdsmi.amdsmi_shut_down()
+    except Exception:          # the tool library is optional: report what is known
+        info["market_name"] = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                info["host_cpu"] = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return info
+
+
+def clock_window(fn, seconds=1.0):
+    """Run fn back to back for about `seconds` while another thread samples the
+    current gfx clock of every XCD (amdsmi GPU metrics); returns the median
+    over samples of the mean XCD clock in MHz, or None without amdsmi."""
+    import threading
+    import torch
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        h = amdsmi.amdsmi_get_processor_handles()[0]
+    except Exception:
+        return None
+    samples, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+                clk = [c for c in m.get("current_gfxclks", []) if isinstance(c, (int, float)) and 0 < c < 10000]
+                if clk:
+                    samples.append(sum(clk) / len(clk))
+            except Exception:
+                pass
+            time.sleep(0.01)
+    try:
+        fn()
+        torch.cuda.synchronize()
+        t = threading.Thread(target=poll)
+        t.start()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(20):
+                fn()
+            torch.cuda.synchronize()
+        stop.set()
+        t.join()
+    finally:
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
+    if not samples:
+        return None
+    samples.sort()
+    return samples[len(samples) // 2]
+
+
+def digest(*tensors):
+    """SHA-256 (first 16 hex digits) of the raw bytes of host or device tensors."""
+    import hashlib
+    import torch
+    h = hashlib.sha256()
+    for t in tensors:
+        t = t.detach().contiguous()
+        if t.dtype in (torch.bfloat16, torch.float8_e4m3fn):
+            t = t.view(torch.uint8)
+        h.update(t.cpu().numpy().tobytes())
+    return h.hexdigest()[:16]
+
+
+def pool_digest(p):
+    """Digest of a paged pool: q, block table, contexts, and one int64 sum of
+    the raw 16-bit words of every page of each cache (computed on the device;
+    hashing 17 GB of pages byte by byte on the host would take minutes)."""
+    import torch
+    sums = [c.view(torch.int16).sum(dim=(1, 2, 3), dtype=torch.int64) for c in (p.kcache, p.vcache)]
+    return digest(p.q, p.block_table, p.ctx_lens, *sums)
+
+
+def decode_cpu_baseline(p, budget_s=10.0):
+    """Time the fp64 oracle's paged decode on whole sequences of the decode
+    workload (all heads), taken in sequence order until about budget_s of
+    oracle time; GB/s = K and V bytes of their contexts / time (the gather of
+    each sequence's pages to the host is not timed)."""
+    import numpy as np
+    import torch
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    ctx = p.ctx_lens.cpu().numpy()
+    bt = p.block_table.cpu().numpy()
+    S, H, d = p.q.shape
+    bits = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    seconds, nbytes, done = 0.0, 0, []
+    for s in range(S):
+        nb = (int(ctx[s]) + 15) // 16
+        pages = torch.from_numpy(bt[s, :nb].astype(np.int64)).to(p.kcache.device)
+        kc, vc = bits(p.kcache.index_select(0, pages)), bits(p.vcache.index_select(0, pages))
+        qf = oracle.bf16_bits_to_f64(bits(p.q[s:s + 1]))
+        table = np.arange(nb, dtype=np.int32)[None, :]
+        t0 = time.perf_counter()
+        oracle.paged_decode(qf, kc, vc, table, ctx[s:s + 1], p.scale)
+        seconds += time.perf_counter() - t0
+        nbytes += int(ctx[s]) * H * d * 2 * 2
+        done.append(int(s))
+        if seconds >= budget_s:
+            break
+    return {"value": nbytes / seconds / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "fp64 oracle paged decode of %d whole sequences (all %d heads; contexts %d..%d, "
+                      "%.3g B of K and V, %.1f s)" % (len(done), H, int(ctx[done].min()), int(ctx[done].max()),
+                                                      nbytes, seconds)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -149,7 +291,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--only", default="",
                     help="comma list of prefill,fp8,decode,backward,paged_prefill,block_sparse,"
-                         "fp8_quantize (default all)")
+                         "fp8_quantize,mha (default all)")
+    ap.add_argument("--no-clock", action="store_true", help="skip the clock-sampling window")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -164,27 +307,31 @@ def main():
     from exact_attention_106_amd import inputs
 
     only = set(filter(None, args.only.split(","))) or {"prefill", "fp8", "decode", "backward", "paged_prefill",
-                                                         "block_sparse", "fp8_quantize"}
+                                                         "block_sparse", "fp8_quantize", "mha"}
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     fa.fa_version()
 
     log("generating inputs")
     parts = []
+    digests = {}
     if "prefill" in only:
         x3 = inputs.config3()
+        digests["causal_bf16_B1H32N16384d128"] = digest(x3.q, x3.k, x3.v)
         q3, k3, v3 = x3.q.to(dev), x3.k.to(dev), x3.v.to(dev)
         o3 = torch.empty_like(q3)
         l3 = torch.empty(q3.shape[:3], dtype=torch.float32, device=dev)
         parts.append(("prefill", lambda: fa.fa_fwd(q3, k3, v3, scale=x3.scale, causal=True, out=o3, lse=l3)))
     if "fp8" in only:
         x4 = inputs.config4()
+        digests["causal_fp8_B2H16N8192d128"] = digest(x4.q8, x4.k8, x4.v8, x4.q_scale, x4.k_scale, x4.v_scale)
         t4 = [t.to(dev) for t in (x4.q8, x4.k8, x4.v8, x4.q_scale, x4.k_scale, x4.v_scale)]
         o4 = torch.empty(x4.q8.shape, dtype=torch.bfloat16, device=dev)
         l4 = torch.empty(x4.q8.shape[:3], dtype=torch.float32, device=dev)
         parts.append(("fp8", lambda: fa.fa_fwd_fp8(*t4, scale=x4.scale, causal=True, out=o4, lse=l4)))
     if "decode" in only:
         p5 = inputs.config5(device=dev)
+        digests["paged_decode_S64H32d128"] = pool_digest(p5)
         ws = torch.empty(fa.fa_paged_decode_workspace_bytes(64, 32, 128, 16, p5.block_table.shape[1]),
                          dtype=torch.uint8, device=dev)
         o5 = torch.empty(p5.q.shape, dtype=torch.bfloat16, device=dev)
@@ -235,6 +382,13 @@ def main():
             for i, (x, rot) in enumerate(zip(xz, (rz, rz, None))):
                 fa.fa_quantize_fp8(x, rot, codes=cz[i], scales=sz[i])
         parts.append(("fp8_quantize", quantize_qkv))
+    if "mha" in only:
+        x2 = inputs.config2()
+        digests["mha_bf16_B4H16N2048d64"] = digest(x2.q, x2.k, x2.v)
+        q2, k2, v2 = x2.q.to(dev), x2.k.to(dev), x2.v.to(dev)
+        o2 = torch.empty_like(q2)
+        l2 = torch.empty(q2.shape[:3], dtype=torch.float32, device=dev)
+        parts.append(("mha", lambda: fa.fa_fwd(q2, k2, v2, scale=x2.scale, causal=False, out=o2, lse=l2)))
     torch.cuda.synchronize()
 
     log("warmup %d" % args.warmup)
@@ -264,6 +418,10 @@ def main():
         t = sorted(a.elapsed_time(b) / launches for a, b in ev[name])
         q = lambda f: t[min(len(t) - 1, int(round(f * (len(t) - 1))))]
         return {"p10": q(0.1), "median": q(0.5), "p90": q(0.9)}
+    sclk = None
+    if not args.no_clock and "prefill" in only:
+        log("clock window")
+        sclk = clock_window(lambda: fa.fa_fwd(q3, k3, v3, scale=x3.scale, causal=True, out=o3, lse=l3))
     if args.calib_copy_mib:
         src = torch.ones(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -279,7 +437,8 @@ def main():
                       "paged pool with shared prefixes)",
               "config": {"workload": "causal bf16 prefill B1 H32 N16384 d128 + fp8 causal prefill "
                                      "B2 H16 N8192 d128 + paged decode S64 H32 d128 ctx 512..32768",
-                         "global_batch": 1, "seq_len": 16384, "parallelism": "single GPU"}}
+                         "global_batch": 1, "seq_len": 16384, "parallelism": "single GPU"},
+              "device": device_info(dev), "sclk_mhz": sclk, "input_sha256": digests}
     if "prefill" in ms:
         f = prefill_flops(1, 32, 16384, 128, True)
         tf = f / (ms["prefill"] * 1e-3) / 1e12
@@ -289,6 +448,9 @@ def main():
                               "traffic": measured_traffic("pmc_fwd_prefill_bf16_causal_B1H32N16384d128.md"),
                               "kernel": "fwd_kernel3<128,causal,bf16>", "launch_ms": ms["prefill"],
                               "launch_ms_spread": spread("prefill"), "flop_per_launch": f}
+        if sclk:
+            # the same fraction against the peak at the gfx clock measured while the kernel ran
+            result["roofline"]["frac_at_sclk"] = tf / (PEAK_BF16_TFLOPS * sclk / 2400.0)
     if "fp8" in ms:
         f = prefill_flops(2, 16, 8192, 128, True)
         tf = f / (ms["fp8"] * 1e-3) / 1e12
@@ -367,11 +529,23 @@ def main():
                                                "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
                                                "traffic": measured_traffic("pmc_fp8_quantize_B2H16N8192d128.md"),
                                                "kernel": "fp8_quant_kernel"}}
+    if "mha" in ms:
+        f = prefill_flops(4, 16, 2048, 64, False)
+        tf = f / (ms["mha"] * 1e-3) / 1e12
+        result["mha"] = {"value": tf, "unit": "TFLOP/s", "launch_ms": ms["mha"], "launch_ms_spread": spread("mha"),
+                         "flop_per_launch": f, "workload": "non-causal bf16 MHA B4 H16 N2048 d64",
+                         "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                      "frac": tf / PEAK_BF16_TFLOPS,
+                                      "traffic": measured_traffic("pmc_fwd_mha_bf16_B4H16N2048d64.md"),
+                                      "kernel": "fwd_kernel3<64,non-causal,bf16>"}}
     if result["value"] is None and "decode" in result:
         result["value"], result["unit"] = result["decode"]["value"], "GB/s"
     if not args.no_cpu_baseline and "prefill" in only:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(x3, args.cpu_budget)
+    if not args.no_cpu_baseline and "decode" in only:
+        log("cpu baseline (oracle paged decode)")
+        result["decode"]["cpu_baseline"] = decode_cpu_baseline(p5, args.cpu_budget / 2)
     print(json.dumps(result), flush=True)
 
 
