@@ -18,8 +18,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ["api.hip", "fwd_f32.hip", "fwd_prefill.hip", "decode.hip", "bwd.hip", "block_manager.hip",
-           "fwd_sparse.hip", "fp8_quant.hip"]
+# the prefill kernel template (fwd_prefill.h) is instantiated in four units
+# that compile in parallel
+SOURCES = ["api.hip", "fwd_f32.hip", "fwd_prefill_bf16.hip", "fwd_prefill_bf16_d64.hip", "fwd_prefill_fp8.hip",
+           "fwd_prefill_paged.hip", "decode.hip", "bwd.hip", "block_manager.hip", "fwd_sparse.hip", "fp8_quant.hip"]
 ARCH = "gfx950"
 
 
@@ -47,7 +49,9 @@ def common_flags():
 # softmax, and shuffle O between AGPRs around the rescale branch; measured:
 # the block-sparse forward runs 16 % faster this way, the paged prefill 9 %
 # slower, so that one keeps the default)
-EXTRA = {"fwd_prefill.hip": ["-fno-honor-nans"],
+PREFILL_FLAGS = ["-fno-honor-nans"]
+EXTRA = {"fwd_prefill_bf16.hip": PREFILL_FLAGS, "fwd_prefill_bf16_d64.hip": PREFILL_FLAGS,
+         "fwd_prefill_fp8.hip": PREFILL_FLAGS, "fwd_prefill_paged.hip": PREFILL_FLAGS,
          "bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
          "fwd_sparse.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
@@ -63,7 +67,7 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    jobs = min(len(SOURCES), int(os.environ.get("MAX_JOBS", "8")))
+    jobs = min(len(SOURCES), int(os.environ.get("MAX_JOBS", str(os.cpu_count() or 8))))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp%d" % os.getpid()

@@ -1,5 +1,6 @@
 // Fused attention forward on gfx950 MFMA: bf16 (d = 64, 128) and FP8 E4M3
-// with per-block scales (d = 128), one kernel template for both.
+// with per-block scales (d = 128), one kernel template for both. The
+// instantiations live in fwd_prefill_{bf16,bf16_d64,fp8,paged}.hip.
 //
 // Work decomposition (FlashAttention-2 parallelisation, 91haoming.cn article,
 // "FlashAttention v2 / parallelisation improvements"; "Flash Attention 再学习",
@@ -55,6 +56,8 @@
 // the context arrive as zeros. Page ids are read one step ahead with scalar
 // loads. With an arbitrary offset between query and key positions a wave may
 // need the mask on two tiles; a query that sees no key gets O = 0, L = -inf.
+#pragma once
+
 #include "fa_device.h"
 #include "fa_dma.h"
 #include "fa_launch.h"
@@ -65,6 +68,10 @@ namespace fa {
 namespace {
 
 constexpr int kBR = 256;       // query rows per workgroup
+// bound on a lane's sum of weights 2^(t - m) over its keys of a tile, past
+// which the tile is redone against its exact row max (2^kRescaleSlack)
+constexpr float kWeightBound = 1048576.f;
+static_assert(kRescaleSlack == 20.f, "kWeightBound is 2^kRescaleSlack");
 constexpr int kBC = 64;        // keys per tile
 constexpr int kScaleBlock = 128;
 
@@ -187,7 +194,7 @@ constexpr int fma_slot(int E) {
     return E < 32 ? elem_slot<MX + 1, NS_PV - MX - 1>(E) : elem_slot<NS_PV, NS_QK / 2>(E - 32);
 }
 template <int MX, int NS_PV, int NS_QK>
-constexpr int exp_slot(int E) {
+constexpr int exp_slot_raw(int E) {
     // fp8: a QK slot lasts two PV slots; spread in time
     const int WQ = NS_QK < NS_PV ? 2 : 1;
     const int u0 = MX + 2, u1 = NS_PV + (NS_QK - 2) * WQ;
@@ -200,6 +207,17 @@ constexpr int exp_slot(int E) {
     const int need = 2 * (c * DT + DT - 1) + 1;
     const int m1 = even > after ? even : after;
     return m1 > need ? m1 : need;
+}
+// the exp slots, made non-decreasing in E (the pack constraint can push an
+// element past its successors' even-spread slots)
+template <int MX, int NS_PV, int NS_QK>
+constexpr int exp_slot(int E) {
+    int r = 0;
+    for (int e = 0; e <= E; ++e) {
+        const int v = exp_slot_raw<MX, NS_PV, NS_QK>(e);
+        r = v > r ? v : r;
+    }
+    return r;
 }
 template <int MX, int NS_PV, int NS_QK>
 constexpr int exp_first(int s) {
@@ -558,13 +576,22 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
     // next PV; ISSUE: the copies of step j. PH = j & 3 when known (the LDS
     // stages then go into the instructions' offset fields), else -1.
     auto block = [&](int j, bool masked, auto has_pv_c, auto has_qk_c, auto has_sm_c, auto pref_c,
-                     auto issue_c, auto phc) __attribute__((always_inline)) {
+                     auto issue_c, auto phc, auto exact_c) __attribute__((always_inline)) {
         constexpr bool HAS_PV = decltype(has_pv_c)::value;
         constexpr bool HAS_QK = decltype(has_qk_c)::value;
         constexpr bool HAS_SM = decltype(has_sm_c)::value;
         constexpr bool PREF = decltype(pref_c)::value;
         constexpr bool ISSUE = decltype(issue_c)::value;
         constexpr int PH = decltype(phc)::value;
+        // EXACT: the tile's row max sets the reference (the first tile, which
+        // holds key 0 and so a visible key of every query that has one).
+        // Otherwise the weights are formed against the current reference and
+        // checked afterwards (see the end of the block). FP8 keeps the exact
+        // max on every tile: with outliers in Q and K (the FP8 workload) some
+        // row of a 64-row wave passed the bound often enough that redoing the
+        // wave's tile cost more than the max it saves (measured 29 % slower).
+        constexpr bool EXACT = decltype(exact_c)::value || FP8;
+        constexpr int MXS = EXACT ? MX : 0;   // slots of the row max
         constexpr int NF = NFV + NFK + PRE;
         constexpr int KIMM = PH < 0 ? 0 : ((PH + 1) & (kRing - 1)) * L::K_TILE;
         constexpr int VIMM = PH < 0 ? 0 : ((PH + kRing - 1) & (kRing - 1)) * L::V_TILE;
@@ -626,6 +653,16 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
         float mu[2] = {0.f, 0.f};
         float x[2][2][16];
         float rsum[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+        [[maybe_unused]] const float lsum_prev[2] = {lsum[0], lsum[1]};
+        [[maybe_unused]] float rs_tile[2] = {0.f, 0.f};   // a lane's sum of this tile's weights
+        [[maybe_unused]] bool over = false;   // a lane's weights of this tile passed the bound
+        if constexpr (HAS_SM && !EXACT) {
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                mu[g] = m[g] == neg_inf() ? 0.f : m[g];
+                if constexpr (FP8) mu[g] -= lps;
+            }
+        }
         // S was written by the MFMAs at the end of the previous block: cover
         // the MFMA-write -> VALU-access distance before the softmax touches it
         // (the fp8 QK MFMA has 16 passes, the bf16 one 8)
@@ -676,7 +713,7 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
             if constexpr (HAS_SM) {
                 // row max of the 32 scores of a lane as a tree of v_max3:
                 // 11 ops in slots [0, MX-2), 4 in slot MX-2, 2 in slot MX-1
-                if constexpr (s < MX - 2) {
+                if constexpr (EXACT && s < MX - 2) {
                     constexpr int a0 = s * 11 / (MX - 2), a1 = (s + 1) * 11 / (MX - 2);
 #pragma unroll
                     for (int gg = 0; gg < 2; ++gg)
@@ -690,7 +727,7 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
                                 mt[gg][a] = fmaxf(sacc[gg][1][14], sacc[gg][1][15]);
                         }
                 }
-                if constexpr (s == MX - 2) {
+                if constexpr (EXACT && s == MX - 2) {
 #pragma unroll
                     for (int gg = 0; gg < 2; ++gg) {
                         mt[gg][0] = max3f(mt[gg][0], mt[gg][1], mt[gg][2]);
@@ -699,12 +736,12 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
                         mt[gg][9] = fmaxf(mt[gg][9], mt[gg][10]);
                     }
                 }
-                if constexpr (s == MX - 1) {
+                if constexpr (EXACT && s == MX - 1) {
 #pragma unroll
                     for (int gg = 0; gg < 2; ++gg)
                         mx[gg] = fmaxf(max3f(mt[gg][0], mt[gg][3], mt[gg][6]), mt[gg][9]);
                 }
-                if constexpr (s == MX) {
+                if constexpr (EXACT && s == MX) {
 #pragma unroll
                     for (int gg = 0; gg < 2; ++gg) {
                         const float mxc = other_half_max(mx[gg]) * ctj[gg];
@@ -724,11 +761,11 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
                 // rewritten from there on), of keys 32..63 in the first half of
                 // the QK slots; the exps, sums and packs of all 64 follow one
                 // even spread over the rest of the block
-                constexpr int S1 = MX + 1, W1 = NS_PV - MX - 1;
+                constexpr int S1 = MXS + 1, W1 = NS_PV - MXS - 1;
                 constexpr int S2 = NS_PV, W2 = NS_QK / 2;
-                static_assert(spread_ok<MX, NS_PV, NS_QK, DT>(), "softmax slot schedule");
+                static_assert(spread_ok<MXS, NS_PV, NS_QK, DT>(), "softmax slot schedule");
                 if constexpr (NS_QK < NS_PV) {
-                    constexpr int F0 = fma_first<MX, NS_PV, NS_QK>(s), F1 = fma_first<MX, NS_PV, NS_QK>(s + 1);
+                    constexpr int F0 = fma_first<MXS, NS_PV, NS_QK>(s), F1 = fma_first<MXS, NS_PV, NS_QK>(s + 1);
 #pragma unroll
                     for (int E = F0; E < F1; ++E)
                         x[(E & 31) / 16][E / 32][E % 16] =
@@ -741,8 +778,8 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
                     for (int e = elem_first<S2, W2>(s); e < elem_first<S2, W2>(s + 1); ++e)
                         x[e / 16][1][e % 16] = fmaf(sacc[e / 16][1][e % 16], ctj[e / 16], -mu[e / 16]);
                 }
-                constexpr int X0 = exp_first<MX, NS_PV, NS_QK>(s - 1), X1 = exp_first<MX, NS_PV, NS_QK>(s),
-                              X2 = exp_first<MX, NS_PV, NS_QK>(s + 1);
+                constexpr int X0 = exp_first<MXS, NS_PV, NS_QK>(s - 1), X1 = exp_first<MXS, NS_PV, NS_QK>(s),
+                              X2 = exp_first<MXS, NS_PV, NS_QK>(s + 1);
 #pragma unroll
                 for (int E = X1; E < X2; ++E)
                     x[(E & 31) / 16][E / 32][E % 16] = exp2_hw(x[(E & 31) / 16][E / 32][E % 16]);
@@ -757,8 +794,17 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
                 }
                 if constexpr (s == NS - 1) {
 #pragma unroll
-                    for (int gg = 0; gg < 2; ++gg)
-                        lsum[gg] += FP8 ? (rsum[gg][0] + rsum[gg][1]) * ipsj : rsum[gg][0] + rsum[gg][1];
+                    for (int gg = 0; gg < 2; ++gg) {
+                        const float rs = FP8 ? (rsum[gg][0] + rsum[gg][1]) * ipsj : rsum[gg][0] + rsum[gg][1];
+                        lsum[gg] += rs;
+                        // every weight of the lane is at most its sum, so a sum
+                        // within the bound keeps each 2^(t - m) <= 2^kRescaleSlack
+                        // (an overflow to inf fails the test as well)
+                        if constexpr (!EXACT) {
+                            rs_tile[gg] = rs;
+                            over = over || !(rs <= kWeightBound);
+                        }
+                    }
                 }
             }
             // fp8: V(j+1), loaded at the start of this block, is widened and
@@ -788,6 +834,118 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
             }
             __builtin_amdgcn_sched_barrier(0);
         });
+        // A lane whose weights passed the bound (its row max grew by more than
+        // kRescaleSlack over the reference, or the sum overflowed): the wave
+        // redoes those rows exactly. S_j is recomputed from K(j), still in its
+        // LDS stage (K(j+4) is copied there only after the next barrier), and
+        // Q; a redone row's max moves its reference, O~ is rescaled at the next
+        // step (moved, alpha) and l restarts from its value before the tile.
+        // Rows whose two half-lanes stayed within the bound keep what the fast
+        // path computed, so a row's result never depends on other rows' keys.
+        if constexpr (HAS_SM && !EXACT) {
+            if (__builtin_amdgcn_ballot_w64(over) != 0) {
+                wait_lgkm<0>();   // every LDS read of the block, the next block's prefetch included
+                if constexpr (PREF) {
+#pragma unroll
+                    for (int p = 0; p < PRE; ++p) asm volatile("" : "+v"(nlo[p]), "+v"(nhi[p]));
+                }
+                const uint32_t kb = (uint32_t)(j & (kRing - 1)) * L::K_TILE;
+                f32x16 st[2][2];
+                static_for<2 * KC>([&](auto qc) {
+                    constexpr int q = decltype(qc)::value, kt = q / KC, kc = q % KC;
+                    KF kf;
+                    if constexpr (FP8) {
+                        u32x4 lo8 = ds_b128<kt * 32 * L::KROW>(kb + koff[kc][0]);
+                        u32x4 hi8 = ds_b128<kt * 32 * L::KROW>(kb + koff[kc][1]);
+                        wait_lgkm<0>();
+                        asm volatile("" : "+v"(lo8), "+v"(hi8));
+                        kf = __builtin_shufflevector(lo8, hi8, 0, 1, 2, 3, 4, 5, 6, 7);
+                    } else {
+                        kf = ds_b128<kt * 32 * L::KROW>(kb + koff[kc][0]);
+                        wait_lgkm<0>();
+                        asm volatile("" : "+v"(kf));
+                    }
+                    asm volatile("s_nop 1");
+#pragma unroll
+                    for (int g = 0; g < 2; ++g) {
+                        if constexpr (kc == 0) mfma_s_first(st[g][kt], kf, qa[g][kc]);
+                        else mfma_s(st[g][kt], kf, qa[g][kc]);
+                    }
+                    // the next fragment's LDS read may land in kf's registers
+                    // (the compiler takes the asm MFMAs as done with them at
+                    // issue): let both MFMAs (the second starts when the first
+                    // ends; 16 passes each for fp8, 8 for bf16) read them first
+                    if constexpr (FP8)
+                        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\t"
+                                     "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\t"
+                                     "s_nop 7\n\ts_nop 7");
+                    else
+                        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\t"
+                                     "s_nop 7\n\ts_nop 7");
+                });
+                if constexpr (FP8) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3");
+                else asm volatile("s_nop 7\n\ts_nop 7");
+                // the compiler takes asm results as ready at once and would hoist
+                // their reads above the nops: pin them after the wait
+#pragma unroll
+                for (int g = 0; g < 2; ++g) asm volatile("" : "+v"(st[g][0]), "+v"(st[g][1]));
+                if (masked) {
+                    const int k0 = j * kBC;
+#pragma unroll
+                    for (int g = 0; g < 2; ++g) {
+                        const int lim =
+                            (CAUSAL ? min(base_pos + qw + 32 * g + l32, kmax - 1) : kmax - 1) - (k0 + 4 * hf);
+#pragma unroll
+                        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                            for (int i = 0; i < 16; ++i)
+                                if (kt * 32 + 8 * (i >> 2) + (i & 3) > lim) st[g][kt][i] = neg_inf();
+                    }
+                }
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {
+                    // the row is redone iff either half-lane's sum passed the bound
+                    // (sums of non-negative weights: inf at worst, never NaN)
+                    const bool redo = !(other_half_max(rs_tile[g]) <= kWeightBound);
+                    float mxl = neg_inf();
+#pragma unroll
+                    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) mxl = fmaxf(mxl, st[g][kt][i]);
+                    const float mxc = other_half_max(mxl) * ctj[g];
+                    const bool move = redo && mxc > m[g];
+                    const float m_new = move ? mxc : m[g];
+                    alpha[g] = move ? exp2_hw(m[g] - m_new) : 1.f;
+                    moved[g] = __builtin_amdgcn_ballot_w64(move) != 0;
+                    m[g] = m_new;
+                    // the redone values replace the fast path's by selection (no
+                    // branch: the hand-scheduled code around stays one region)
+                    float mug = m_new == neg_inf() ? 0.f : m_new;
+                    if constexpr (FP8) mug -= lps;
+                    float rs = 0.f;
+                    bf16x8 pn[4];
+#pragma unroll
+                    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                        for (int i = 0; i < 16; i += 2) {
+                            const float p0 = exp2_hw(fmaf(st[g][kt][i], ctj[g], -mug));
+                            const float p1 = exp2_hw(fmaf(st[g][kt][i + 1], ctj[g], -mug));
+                            rs += p0 + p1;
+                            pn[2 * kt + (i >> 3)][i & 7] = (__bf16)p0;
+                            pn[2 * kt + (i >> 3)][(i & 7) + 1] = (__bf16)p1;
+                        }
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const u32x4 a = __builtin_bit_cast(u32x4, pf[g][c]), b = __builtin_bit_cast(u32x4, pn[c]);
+                        u32x4 r;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) r[e] = redo ? b[e] : a[e];
+                        pf[g][c] = __builtin_bit_cast(bf16x8, r);
+                    }
+                    lsum[g] = redo ? lsum_prev[g] * alpha[g] + (FP8 ? rs * ipsj : rs) : lsum[g];
+                }
+            }
+        }
         // reads scheduled past the last slot (next-block prefetch of short blocks)
         static_for<NF>([&](auto fc) {
             constexpr int f = decltype(fc)::value;
@@ -914,17 +1072,17 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
     asm volatile("s_nop 7");
     lds_barrier();
     using G = std::integral_constant<int, -1>;   // LDS stages from j at run time
-    block(-1, false, F{}, T{}, F{}, F{}, F{}, G{});        // S(0) = K(0) Q^T
+    block(-1, false, F{}, T{}, F{}, F{}, F{}, G{}, F{});        // S(0) = K(0) Q^T
 
     // ---- block 0 ----
     mid(0);
-    if (last >= 1) block(0, 0 >= j_mask, F{}, T{}, T{}, T{}, T{}, G{});
-    else block(0, true, F{}, F{}, T{}, T{}, T{}, G{});
+    if (last >= 1) block(0, 0 >= j_mask, F{}, T{}, T{}, T{}, T{}, G{}, T{});
+    else block(0, true, F{}, F{}, T{}, T{}, T{}, G{}, T{});
     // ---- blocks 1 .. last-1 ----
     auto step = [&](int j, auto phc, bool masked) __attribute__((always_inline)) {
         rescale();
         mid(j);
-        block(j, masked, T{}, T{}, T{}, T{}, T{}, phc);
+        block(j, masked, T{}, T{}, T{}, T{}, T{}, phc, F{});
     };
     int j = 1;
     // blocks below j_open need no mask (dense: only `last` can need one)
@@ -940,13 +1098,13 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
     if (last >= 1) {
         rescale();
         mid(last);
-        block(last, last >= j_mask, T{}, F{}, T{}, T{}, T{}, G{});
+        block(last, last >= j_mask, T{}, F{}, T{}, T{}, T{}, G{}, F{});
     }
     // ---- PV(last) with the fragments read ahead by the block before (no
     // step in between, so wait for those reads here) ----
     rescale();
     wait_lgkm<0>();
-    block(last + 1, false, T{}, F{}, F{}, F{}, F{}, G{});
+    block(last + 1, false, T{}, F{}, F{}, F{}, F{}, G{}, F{});
     // causal: the remaining copies are issued for the other waves
     for (int jj = last + 1; jj < n_tiles; ++jj) {
         mid(jj);
@@ -1001,41 +1159,8 @@ hipError_t launch_t(const void *q, const void *k, const void *v, const float *qs
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, void *o, float *lse, int B,
-                           int H, int N, int d, float scale, int causal, hipStream_t stream)
-{
-    if (d == 64)
-        return causal ? launch_t<64, true, false>(q, k, v, nullptr, nullptr, nullptr, o, lse, B, H, N, scale, stream)
-                      : launch_t<64, false, false>(q, k, v, nullptr, nullptr, nullptr, o, lse, B, H, N, scale, stream);
-    return causal ? launch_t<128, true, false>(q, k, v, nullptr, nullptr, nullptr, o, lse, B, H, N, scale, stream)
-                  : launch_t<128, false, false>(q, k, v, nullptr, nullptr, nullptr, o, lse, B, H, N, scale, stream);
-}
-
-// chunked prefill through the block table: the n_new newest tokens of each
-// sequence (q [S, H, n_new, 128]) against its paged cache [pages, H, 16, 128]
-hipError_t launch_paged_prefill_mfma(const void *q, const void *kcache, const void *vcache,
-                                     const int32_t *block_table, const int32_t *ctx_lens, void *o, float *lse,
-                                     int num_seqs, int H, int n_new, int max_blocks_per_seq, float scale,
-                                     hipStream_t stream)
-{
-    const int n_rb = (n_new + kBR - 1) / kBR;
-    const int BH = num_seqs * H;
-    const dim3 grid((unsigned)((size_t)BH * n_rb));
-    const PagedArgs pg{block_table, ctx_lens, (uint64_t)H * 16 * 128 * 2, max_blocks_per_seq, H};
-    hipLaunchKernelGGL((fwd_kernel3<128, true, false, true>), grid, dim3(kThreads3), 0, stream,
-                       static_cast<const uint8_t *>(q), static_cast<const uint8_t *>(kcache),
-                       static_cast<const uint8_t *>(vcache), nullptr, nullptr, nullptr, static_cast<uint16_t *>(o),
-                       lse, n_new, BH, n_rb, scale * kLog2e, pg);
-    return hipGetLastError();
-}
-
-hipError_t launch_fwd_fp8(const uint8_t *q8, const uint8_t *k8, const uint8_t *v8, const float *qs,
-                          const float *ks, const float *vs, void *o, float *lse, int B, int H, int N,
-                          int d, float scale, int causal, hipStream_t stream)
-{
-    (void)d;
-    return causal ? launch_t<128, true, true>(q8, k8, v8, qs, ks, vs, o, lse, B, H, N, scale, stream)
-                  : launch_t<128, false, true>(q8, k8, v8, qs, ks, vs, o, lse, B, H, N, scale, stream);
-}
+// bf16 forward with d = 64 (its own translation unit, compiled in parallel)
+hipError_t launch_fwd_bf16_d64(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+                               int N, float scale, int causal, hipStream_t stream);
 
 }  // namespace fa

@@ -336,3 +336,49 @@ def test_decode_S64H32d128_full_size_sampled(fa, gpu):
         ro, rl = oracle.paged_decode(f64_bf16(p.q[s:s + 1]), kc, vc, table, ctx[s:s + 1], p.scale)
         assert_close("decode seq %d ctx %d" % (s, ctx[s]), f64_bf16(o[s:s + 1]),
                      l[s:s + 1].cpu().double().numpy(), ro, rl, 2e-2, 1e-3)
+
+
+# ---------------------------------------------------------------------------------- reference jumps
+
+@pytest.mark.parametrize("d,causal", [(128, True), (128, False), (64, True), (64, False)])
+def test_bf16_score_jumps_redo_the_tile_exactly(fa, gpu, d, causal):
+    # After the first tile the kernel forms 2^(t - m) against the running
+    # reference and redoes a tile exactly when a lane's weights pass 2^20.
+    # Key 700 aligned with query 800 (x10) gives a score far past the first
+    # tiles' (2^(t - m) overflows to inf on the fast path), and keys 300..363
+    # scaled x8 raise many rows' maxima by more than 2^20.
+    x = inputs.dense(1, 2, 1000, d, seed=4000 + d + causal, dtype="bf16")
+    k = x.k.clone()
+    k[:, :, 700] = (x.q[:, :, 800].float() * 10).to(torch.bfloat16)
+    k[:, :, 300:364] = (k[:, :, 300:364].float() * 8).to(torch.bfloat16)
+    log("fa_fwd bf16 score jumps d%d causal=%d" % (d, causal))
+    o, l = fa.fa_fwd(x.q.to(gpu), k.to(gpu), x.v.to(gpu), scale=x.scale, causal=causal)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention(f64_bf16(x.q), f64_bf16(k), f64_bf16(x.v), x.scale, causal)
+    assert_close("bf16 score jumps", f64_bf16(o), l.cpu().double().numpy(), ro, rl, 2e-2, 1e-3)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_score_jumps(fa, gpu, causal):
+    # a K scale block x64 (keys 256..383): scores of those keys jump far past
+    # the first tiles' for every query that sees them (the reference moves by
+    # more than 2^20 within a row). The FP8 Q.K^T products carry a relative
+    # error of a few 1e-4 (the E4M3 dot products of the MFMA; the same inputs
+    # at x1 already give an L error of 1.6e-3 on one row of 2000), which grows
+    # with the scores: L is held to 1e-3 relative to |L| here, O to the FP8 bound.
+    x = inputs.fp8_inputs(1, 2, 1000, 128, seed=4100 + causal, causal=causal)
+    ks = x.k_scale.clone()
+    ks[:, :, 2] *= 64.0
+    log("fa_fwd_fp8 score jumps causal=%d" % causal)
+    o, l = fa.fa_fwd_fp8(x.q8.to(gpu), x.k8.to(gpu), x.v8.to(gpu), x.q_scale.to(gpu), ks.to(gpu),
+                         x.v_scale.to(gpu), scale=x.scale, causal=causal)
+    torch.cuda.synchronize()
+    q = oracle.dequant_e4m3(x.q8.numpy(), x.q_scale.numpy())
+    k = oracle.dequant_e4m3(x.k8.numpy(), ks.numpy())
+    v = oracle.dequant_e4m3(x.v8.numpy(), x.v_scale.numpy())
+    ro, rl = oracle.attention(q, k, v, x.scale, causal)
+    got_l = l.cpu().double().numpy()
+    assert_close("fp8 score jumps", f64_bf16(o), got_l, ro, rl, 8e-2 + half_ulp_bf16(ro), float("inf"))
+    rel = float(np.max(np.abs(got_l - rl) / np.maximum(1.0, np.abs(rl))))
+    log("fp8 score jumps: max |dL| / max(1, |L|) = %.3e" % rel)
+    assert rel <= 1e-3
