@@ -209,16 +209,27 @@ constexpr int exp_slot_raw(int E) {
     return m1 > need ? m1 : need;
 }
 // the exp slots, made non-decreasing in E (the pack constraint can push an
-// element past its successors' even-spread slots)
+// element past its successors' even-spread slots), tabulated once per
+// schedule so that the per-slot lookups stay cheap to compile
 template <int MX, int NS_PV, int NS_QK>
-constexpr int exp_slot(int E) {
-    int r = 0;
-    for (int e = 0; e <= E; ++e) {
-        const int v = exp_slot_raw<MX, NS_PV, NS_QK>(e);
-        r = v > r ? v : r;
+struct ExpSlots {
+    struct Table {
+        signed char v[64];
+    };
+    static constexpr Table make() {
+        Table t{};
+        int r = 0;
+        for (int e = 0; e < 64; ++e) {
+            const int v = exp_slot_raw<MX, NS_PV, NS_QK>(e);
+            r = v > r ? v : r;
+            t.v[e] = (signed char)r;
+        }
+        return t;
     }
-    return r;
-}
+    static constexpr Table table = make();
+};
+template <int MX, int NS_PV, int NS_QK>
+constexpr int exp_slot(int E) { return ExpSlots<MX, NS_PV, NS_QK>::table.v[E]; }
 template <int MX, int NS_PV, int NS_QK>
 constexpr int exp_first(int s) {
     int E = 0;
