@@ -56,67 +56,112 @@ __device__ __forceinline__ void merge_into(State &a, float m2, float l2, const f
 
 // ---- prefix sharing between sequences (PagedAttention section) ----
 // Two sequences whose block tables name the same 32 pages for a full chunk
-// read those pages once: the lower-ranked of a pair computes both queries'
-// partials. Pairs are formed in sequence order inside each class of equal
-// chunks (members m0 < m1 < m2 ...: (m0, m1), (m2, m3), ...).
-// pair[s][c] = partner index, -1 alone, -2 handled by the partner.
+// read those pages once: one workgroup computes both queries' partials.
+// Chunks are grouped into classes of equal page lists with a hash table
+// (expected O(1) work per chunk, any number of sequences), and the members of
+// a class are paired two by two. Which members end up paired does not change
+// any result: a query's partial is computed by the same operations alone or
+// in a pair. pair[s][c] = partner sequence, -1 alone, -2 handled by the partner.
+//
 // every slot of chunk c lies inside sequence s's context
 __device__ __forceinline__ bool chunk_full(const int32_t *ctx_lens, int s, int c) {
     return (c + 1) * kPPS * kPS <= ctx_lens[s];
 }
-__global__ __launch_bounds__(256) void decode_hash_kernel(const int32_t *__restrict__ block_table,
-                                                          const int32_t *__restrict__ ctx_lens,
-                                                          uint64_t *__restrict__ hash, int *__restrict__ n_pairs,
-                                                          int S, int max_blocks, int max_splits) {
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i == 0) *n_pairs = 0;   // the pair list of this call starts empty
-    if (i >= S * max_splits) return;
-    const int s = i / max_splits, c = i % max_splits;
-    uint64_t hv = 0;   // 0 marks "not a full chunk"
-    if (chunk_full(ctx_lens, s, c)) {
-        const int32_t *e = block_table + (size_t)s * max_blocks + c * kPPS;
-        hv = 1469598103934665603ull;   // FNV-1a over the 32 entries
-        for (int k = 0; k < kPPS; ++k) {
-            hv ^= (uint32_t)e[k];
-            hv *= 1099511628211ull;
-        }
-        hv |= 1;
-    }
-    hash[i] = hv;
+// the 32 block-table entries of chunk c of sequence s
+__device__ __forceinline__ const int32_t *chunk_entries(const int32_t *block_table, int max_blocks, int s, int c) {
+    return block_table + (size_t)s * max_blocks + c * kPPS;
 }
+// Per chunk: its hash (0: not a full chunk) and pair slot; the hash table and
+// the pair count are cleared for this call.
+__global__ __launch_bounds__(256) void decode_plan_kernel(const int32_t *__restrict__ block_table,
+                                                          const int32_t *__restrict__ ctx_lens,
+                                                          uint64_t *__restrict__ hash, int *__restrict__ pair,
+                                                          unsigned long long *__restrict__ tab,
+                                                          int *__restrict__ waiting, int *__restrict__ n_pairs,
+                                                          int S, int max_blocks, int max_splits, int T) {
+    const int n_chunks = S * max_splits;
+    const int n = n_chunks > T ? n_chunks : T;
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) {
+        if (i == 0) *n_pairs = 0;
+        if (i < T) {
+            tab[i] = 0ull;
+            waiting[i] = -1;
+        }
+        if (i < n_chunks) {
+            const int s = i / max_splits, c = i % max_splits;
+            uint64_t hv = 0;
+            if (chunk_full(ctx_lens, s, c)) {
+                const int32_t *e = chunk_entries(block_table, max_blocks, s, c);
+                hv = 1469598103934665603ull;   // FNV-1a over the chunk index and its 32 entries
+                hv ^= (uint32_t)c;
+                hv *= 1099511628211ull;
+                for (int k = 0; k < kPPS; ++k) {
+                    hv ^= (uint32_t)e[k];
+                    hv *= 1099511628211ull;
+                }
+                hv |= 1;
+            }
+            hash[i] = hv;
+            pair[i] = -1;
+        }
+    }
+}
+// Per full chunk i = s * max_splits + c: find its class in the hash table (a
+// slot holds the upper 32 bits of the hash and the first member; a member
+// whose page list differs from the slot's first member goes on probing), then
+// pair with the member parked at the slot, or park there. T is a power of two
+// of at least twice the chunk count, so probing ends at a free slot.
 __global__ __launch_bounds__(256) void decode_pair_kernel(const int32_t *__restrict__ block_table,
                                                           const uint64_t *__restrict__ hash,
-                                                          int *__restrict__ pair, int *__restrict__ n_pairs,
+                                                          int *__restrict__ pair,
+                                                          unsigned long long *__restrict__ tab,
+                                                          int *__restrict__ waiting, int *__restrict__ n_pairs,
                                                           int *__restrict__ pair_list, int S, int max_blocks,
-                                                          int max_splits) {
+                                                          int max_splits, int T) {
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i >= S * max_splits) return;
-    const int s = i / max_splits, c = i % max_splits;
     const uint64_t hv = hash[i];
-    int res = -1;
-    if (hv != 0) {
-        const int32_t *e = block_table + (size_t)s * max_blocks + c * kPPS;
-        auto same = [&](int t) {
-            if (hash[(size_t)t * max_splits + c] != hv) return false;
-            const int32_t *f = block_table + (size_t)t * max_blocks + c * kPPS;
-            for (int k = 0; k < kPPS; ++k)
-                if (f[k] != e[k]) return false;
-            return true;
-        };
-        int rank = 0;
-        for (int t = 0; t < s; ++t) rank += same(t);
-        if (rank & 1) {
-            res = -2;
-        } else {
-            for (int t = s + 1; t < S; ++t)
-                if (same(t)) {
-                    res = t;
-                    break;
-                }
+    if (hv == 0) return;
+    const int s = i / max_splits, c = i % max_splits;
+    const int32_t *e = chunk_entries(block_table, max_blocks, s, c);
+    const uint32_t key = (uint32_t)(hv >> 32);
+    const unsigned long long mine = ((unsigned long long)key << 32) | (unsigned long long)(uint32_t)(i + 1);
+    int slot = -1;
+    for (int probe = 0, t = (int)(hv & (uint64_t)(T - 1)); probe < T; ++probe, t = (t + 1) & (T - 1)) {
+        const unsigned long long old = atomicCAS(&tab[t], 0ull, mine);
+        if (old == 0ull) {   // a new class, this chunk its first member
+            slot = t;
+            break;
+        }
+        if ((uint32_t)(old >> 32) != key) continue;
+        const int first = (int)(uint32_t)old - 1;   // chunk index of the slot's first member
+        if (first % max_splits != c) continue;
+        const int32_t *f = chunk_entries(block_table, max_blocks, first / max_splits, c);
+        bool same = true;
+        for (int k = 0; k < kPPS; ++k) same = same && f[k] == e[k];
+        if (same) {
+            slot = t;
+            break;
         }
     }
-    pair[i] = res;
-    if (res >= 0) pair_list[atomicAdd(n_pairs, 1)] = i;   // (s, c) of a pair leader
+    if (slot < 0) return;   // not reached (a free slot always exists): the chunk stays alone
+    // pair with the parked member or park: every successful exchange ends one
+    // member's loop, so the loop ends; the bound only guards against misuse
+    int partner = -1;
+    for (int it = 0; it < (1 << 20); ++it) {
+        const int cur = __hip_atomic_load(&waiting[slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (cur < 0) {
+            if (atomicCAS(&waiting[slot], -1, i) == -1) break;   // parked; a later member may pair with it
+        } else if (atomicCAS(&waiting[slot], cur, -1) == cur) {
+            partner = cur;
+            break;
+        }
+    }
+    if (partner < 0) return;
+    const int lead = min(i, partner), follow = max(i, partner);
+    pair[lead] = follow / max_splits;   // the partner's sequence (same chunk index)
+    pair[follow] = -2;
+    pair_list[atomicAdd(n_pairs, 1)] = lead;
 }
 
 // One (chunk, head, sequence) with NQ = 1 query, or a shared chunk with the
@@ -331,8 +376,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     split_chunk<1>(q, kc, vc, block_table, ctx_lens, ws, H, max_blocks, max_splits, c, split, h, s, s);
 }
 
-// the shared chunks: a fixed grid walks the pair list (its length is only
-// known on the device); every workgroup leaves when the list is done
+// The shared chunks: a fixed grid walks the pair list (its length is only
+// known on the device); every workgroup leaves when the list is done. A
+// kernel of its own, because the two-query path needs about twice the
+// registers of the single one and would halve the split kernel's occupancy.
 constexpr int kPairGrid = 512;
 __global__ __launch_bounds__(256) void decode_pair_split_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc,
@@ -408,21 +455,26 @@ hipError_t launch_paged_decode(const void *q, const void *kcache, const void *vc
     (void)page_size;
     const int max_splits = decode_max_splits(max_blocks_per_seq);
     const int n_chunks = num_seqs * max_splits;
+    const int T = decode_table_slots(num_seqs, max_blocks_per_seq);
     uint8_t *tail = reinterpret_cast<uint8_t *>(workspace) +
                     decode_partials_floats(num_seqs, H, max_blocks_per_seq) * sizeof(float);
     uint64_t *hash = reinterpret_cast<uint64_t *>(tail);
-    int *pair = reinterpret_cast<int *>(tail + (size_t)n_chunks * sizeof(uint64_t));
+    unsigned long long *tab = reinterpret_cast<unsigned long long *>(tail + (size_t)n_chunks * sizeof(uint64_t));
+    int *pair = reinterpret_cast<int *>(tab + T);
     int *pair_list = pair + n_chunks;
-    int *n_pairs = pair_list + n_chunks;
-    const dim3 gp((unsigned)((n_chunks + 255) / 256));
+    int *waiting = pair_list + n_chunks;
+    int *n_pairs = waiting + T;
     const uint16_t *qq = static_cast<const uint16_t *>(q);
     const uint16_t *kk = static_cast<const uint16_t *>(kcache);
     const uint16_t *vv = static_cast<const uint16_t *>(vcache);
     const float c = scale * kLog2e;
-    hipLaunchKernelGGL(decode_hash_kernel, gp, dim3(256), 0, stream, block_table, ctx_lens, hash, n_pairs,
-                       num_seqs, max_blocks_per_seq, max_splits);
-    hipLaunchKernelGGL(decode_pair_kernel, gp, dim3(256), 0, stream, block_table, hash, pair, n_pairs,
-                       pair_list, num_seqs, max_blocks_per_seq, max_splits);
+    const int n_init = n_chunks > T ? n_chunks : T;
+    const dim3 g0((unsigned)min((n_init + 255) / 256, 4096));
+    hipLaunchKernelGGL(decode_plan_kernel, g0, dim3(256), 0, stream, block_table, ctx_lens, hash, pair, tab, waiting,
+                       n_pairs, num_seqs, max_blocks_per_seq, max_splits, T);
+    const dim3 gp((unsigned)((n_chunks + 255) / 256));
+    hipLaunchKernelGGL(decode_pair_kernel, gp, dim3(256), 0, stream, block_table, hash, pair, tab, waiting, n_pairs,
+                       pair_list, num_seqs, max_blocks_per_seq, max_splits, T);
     // heads on x where the chunk count fits the y dimension (65535; x has no
     // such limit), else chunks on x
     const int head_fastest = max_splits <= 65535 ? 1 : 0;
@@ -485,8 +537,9 @@ hipError_t launch_paged_decode_noalloc(const void *q, const void *kcache, const 
     const hipError_t e = scratch_address(&ws);
     if (e != hipSuccess) return e;
     // every word of the workspace the kernels read is written earlier in the
-    // same call (partials, hashes, pair slots; the pair count is reset by the
-    // first kernel), so the buffer needs no clearing between calls
+    // same call (the first kernel writes the hashes and pair slots and clears
+    // the hash table and the pair count; the partials are written before the
+    // merge reads them), so the buffer needs no clearing between calls
     return launch_paged_decode(q, kcache, vcache, block_table, ctx_lens, o, lse, num_seqs, H, d, page_size,
                                max_blocks_per_seq, scale, static_cast<float *>(ws), stream);
 }

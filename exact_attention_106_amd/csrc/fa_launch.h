@@ -36,16 +36,25 @@ inline int decode_max_splits(int max_blocks_per_seq) {
 // Floats per split partial: m, l, then d unscaled output values.
 inline size_t decode_partial_floats(int d) { return (size_t)d + 2; }
 
-// Workspace: the partials of every (sequence, head, chunk), d = 128, then per
-// (sequence, chunk) a 64-bit hash, a partner index and a pair-list slot, then
-// the pair-list length.
+// Workspace: the partials of every (sequence, head, chunk), d = 128; per
+// (sequence, chunk) a 64-bit hash; the hash table of chunk classes (T 64-bit
+// slots); per (sequence, chunk) a partner index and a pair-list slot; the
+// table's T parking slots; the pair-list length.
 inline size_t decode_partials_floats(int num_seqs, int H, int max_blocks_per_seq) {
     return (size_t)num_seqs * H * decode_max_splits(max_blocks_per_seq) * decode_partial_floats(128);
 }
+// slots of the chunk-class hash table: a power of two, at least twice the chunks
+inline int decode_table_slots(int num_seqs, int max_blocks_per_seq) {
+    const size_t need = 2 * (size_t)num_seqs * decode_max_splits(max_blocks_per_seq);
+    size_t t = 64;
+    while (t < need) t <<= 1;
+    return (int)t;
+}
 inline size_t decode_workspace_bytes(int num_seqs, int H, int max_blocks_per_seq) {
+    const size_t n_chunks = (size_t)num_seqs * decode_max_splits(max_blocks_per_seq);
+    const size_t T = (size_t)decode_table_slots(num_seqs, max_blocks_per_seq);
     return decode_partials_floats(num_seqs, H, max_blocks_per_seq) * sizeof(float) +
-           (size_t)num_seqs * decode_max_splits(max_blocks_per_seq) * (sizeof(uint64_t) + 2 * sizeof(int)) +
-           sizeof(int);
+           n_chunks * (sizeof(uint64_t) + 2 * sizeof(int)) + T * (sizeof(uint64_t) + sizeof(int)) + sizeof(int);
 }
 
 hipError_t launch_fp8_quantize(const void *x, const void *rot, uint8_t *codes, float *scales, int B, int H,

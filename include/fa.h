@@ -162,9 +162,10 @@ fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, con
 /*
  * Bytes of device workspace fa_paged_decode needs for these sizes (the split
  * partials (m, l, unscaled O) of every (sequence, head, KV chunk of 32
- * pages), then per (sequence, chunk) a 64-bit hash and a partner index used
- * to read chunks shared between sequences once). Returns 0 for unsupported
- * sizes.
+ * pages), then per (sequence, chunk) a 64-bit hash, a partner index and a
+ * pair-list slot, and a hash table of chunk classes with twice as many slots
+ * as chunks (rounded up to a power of two), used to read chunks shared
+ * between sequences once). Returns 0 for unsupported sizes.
  */
 size_t fa_paged_decode_workspace_bytes(int num_seqs, int H, int d, int page_size,
                                        int max_blocks_per_seq);

@@ -110,8 +110,9 @@ def test_paged_decode_validation(lib):
     need = lib.fa_paged_decode_workspace_bytes(64, 32, 128, 16, 2048)
     # partials (m, l, 128 outputs) per (sequence, head, 32-page chunk), then a
     # 64-bit hash, a partner index and a pair-list slot per (sequence, chunk),
-    # then the pair-list length
-    assert need == 64 * 32 * 64 * 130 * 4 + 64 * 64 * (8 + 4 + 4) + 4
+    # a hash table of chunk classes (a power of two of at least twice the
+    # chunks, 8-byte slots and 4-byte parking places), then the pair-list length
+    assert need == 64 * 32 * 64 * 130 * 4 + 64 * 64 * (8 + 4 + 4) + 8192 * (8 + 4) + 4
     assert lib.fa_paged_decode_workspace_bytes(64, 32, 64, 16, 2048) == 0
     assert lib.fa_paged_decode_workspace_bytes(64, 32, 128, 8, 2048) == 0
 

@@ -338,6 +338,51 @@ def test_decode_S64H32d128_full_size_sampled(fa, gpu):
                      l[s:s + 1].cpu().double().numpy(), ro, rl, 2e-2, 1e-3)
 
 
+
+def test_decode_S4096_many_sharing_classes(fa, gpu):
+    # 4096 sequences whose first two 32-page chunks come from small sets of page
+    # lists (150 for chunk 0: classes of about 27 members, odd sizes included;
+    # 3000 for chunk 1: mostly single members and pairs), then 1..5 pages of
+    # their own. Grouping the chunk classes at this size must stay cheap and
+    # every query must still see exactly its own pages.
+    S, H, d = 4096, 1, 128
+    rng = np.random.Generator(np.random.PCG64(71))
+    ctx = rng.integers(1025, 1100, size=S, endpoint=True).astype(np.int64)
+    nb = (ctx + 15) // 16
+    n0, n1 = 150, 3000
+    pick0 = rng.integers(0, n0, size=S)
+    pick1 = rng.integers(0, n1, size=S)
+    tails = nb - 64
+    P = 32 * (n0 + n1) + int(tails.sum())
+    perm = rng.permutation(P).astype(np.int32)
+    table = np.full((S, int(nb.max())), -1, dtype=np.int32)
+    nxt = 32 * (n0 + n1)
+    for s in range(S):
+        table[s, :32] = perm[32 * pick0[s]:32 * pick0[s] + 32]
+        table[s, 32:64] = perm[32 * (n0 + pick1[s]):32 * (n0 + pick1[s]) + 32]
+        table[s, 64:nb[s]] = perm[nxt:nxt + tails[s]]
+        nxt += int(tails[s])
+    assert nxt == P
+    g = torch.Generator(device=gpu)
+    g.manual_seed(71)
+    kc = torch.randn((P, H, 16, d), generator=g, device=gpu).to(torch.bfloat16)
+    vc = torch.randn((P, H, 16, d), generator=g, device=gpu).to(torch.bfloat16)
+    q = torch.from_numpy(rng.standard_normal((S, H, d), dtype=np.float32)).to(torch.bfloat16)
+    scale = 1.0 / math.sqrt(d)
+    log("fa_paged_decode S4096 H1 d128, shared chunk classes")
+    o, l = fa.fa_paged_decode(q.to(gpu), kc, vc, torch.from_numpy(table).to(gpu),
+                              torch.from_numpy(ctx.astype(np.int32)).to(gpu), scale=scale)
+    torch.cuda.synchronize()
+    big = np.flatnonzero(pick0 == np.bincount(pick0).argmax())[:9]   # members of one large class
+    seqs = sorted(set(big.tolist()) | set(rng.choice(S, 40, replace=False).tolist()))
+    for s in seqs:
+        pages = torch.from_numpy(table[s, :nb[s]].astype(np.int64)).to(gpu)
+        ro, rl = oracle.paged_decode(f64_bf16(q[s:s + 1]), bits16(kc.index_select(0, pages)),
+                                     bits16(vc.index_select(0, pages)),
+                                     np.arange(nb[s], dtype=np.int32)[None, :], ctx[s:s + 1], scale)
+        assert_close("decode S4096 seq %d" % s, f64_bf16(o[s:s + 1]), l[s:s + 1].cpu().double().numpy(),
+                     ro, rl, 2e-2, 1e-3)
+
 # ---------------------------------------------------------------------------------- reference jumps
 
 @pytest.mark.parametrize("d,causal", [(128, True), (128, False), (64, True), (64, False)])
