@@ -75,6 +75,25 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dot_kernel(const uint16_t *__
     }
 }
 
+// Block of this workgroup: the rank-th block (heaviest first under causal
+// masking) of head bh. Workgroup ids go round-robin over the GPU's 8 XCDs,
+// each with its own L2. When B*H is a multiple of 8, XCD x takes heads x,
+// x + 8, x + 16, ... one after the other and the consecutive ids it receives
+// are consecutive blocks of one head: the 32 or so workgroups that run
+// together on an XCD stream the same head's tiles through its L2, which reads
+// each tile from HBM about once per such group. Otherwise consecutive ids are
+// the heads of one block.
+__device__ __forceinline__ void block_of(int &rank, int &bh, int BH, int n_blocks) {
+    if (BH % 8 == 0) {
+        const int x = blockIdx.x % 8, j = blockIdx.x / 8;
+        rank = j % n_blocks;
+        bh = x + 8 * (j / n_blocks);
+    } else {
+        rank = blockIdx.x / BH;
+        bh = blockIdx.x % BH;
+    }
+}
+
 // S (VGPR, in/out) += A (VGPR) x B (VGPR)
 __device__ __forceinline__ void mfma_acc_v(f32x16 &acc, u32x4 a, u32x4 b) {
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
@@ -99,7 +118,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TILE + 2 * 2 * kBwdTile * 4];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, h = lane >> 5;
-    const int kb = blockIdx.x / BH, bh = blockIdx.x % BH;
+    int kb, bh;
+    block_of(kb, bh, BH, (N + kBwdBlock - 1) / kBwdBlock);
     const int k0 = kb * kBwdBlock;
     const int kw = k0 + 32 * w;
     const int my_key = kw + l32;
@@ -325,7 +345,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
     __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TILE];   // [stage][K, V]
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, h = lane >> 5;
-    const int rank = blockIdx.x / BH, bh = blockIdx.x % BH;
+    int rank, bh;
+    block_of(rank, bh, BH, n_qb);
     const int qb = CAUSAL ? n_qb - 1 - rank : rank;
     const int qw = qb * kBwdBlock + 32 * w;
     const int my_q = qw + l32;
