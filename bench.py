@@ -21,7 +21,10 @@ event time); decode GB/s and fp8 TFLOP/s are reported beside it. The CPU
 baselines are the fp64 oracle, timed on bounded samples of the prefill and
 decode workloads on this host's cores. After the timed steps the headline
 prefill runs back to back for about a second while the GPU's gfx clock is
-sampled (amdsmi), for a clock-adjusted fraction of peak beside the spec one.
+sampled (amdsmi), for a clock-adjusted fraction of peak beside the spec one,
+and then the same launch on all-zero Q, K, V is timed and clocked the same
+way (roofline.zero_inputs): identical instructions and traffic, so the gap
+shows how far the chip's clock drops under MFMAs on random operands.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
@@ -419,9 +422,28 @@ def main():
         q = lambda f: t[min(len(t) - 1, int(round(f * (len(t) - 1))))]
         return {"p10": q(0.1), "median": q(0.5), "p90": q(0.9)}
     sclk = None
+    zero_inputs = None
     if not args.no_clock and "prefill" in only:
         log("clock window")
         sclk = clock_window(lambda: fa.fa_fwd(q3, k3, v3, scale=x3.scale, causal=True, out=o3, lse=l3))
+        # The same kernel, shape and launch on all-zero Q, K, V: the same
+        # instructions and memory traffic, far less switching in the matrix
+        # cores. The gap between the two is the chip lowering its clock under
+        # the power drawn by MFMAs on random operands (context, not a result).
+        zq, zk, zv = (torch.zeros_like(t) for t in (q3, k3, v3))
+        zrun = lambda: fa.fa_fwd(zq, zk, zv, scale=x3.scale, causal=True, out=o3, lse=l3)
+        zclk = clock_window(zrun)
+        za, zb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        za.record(stream)
+        for _ in range(20):
+            zrun()
+        zb.record(stream)
+        torch.cuda.synchronize()
+        zms = za.elapsed_time(zb) / 20
+        ztf = prefill_flops(1, 32, 16384, 128, True) / (zms * 1e-3) / 1e12
+        zero_inputs = {"workload": "causal bf16 prefill B1 H32 N16384 d128 on all-zero Q, K, V",
+                       "launch_ms": zms, "tflops": ztf, "frac": ztf / PEAK_BF16_TFLOPS, "sclk_mhz": zclk}
+        del zq, zk, zv
     if args.calib_copy_mib:
         src = torch.ones(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -451,6 +473,8 @@ def main():
         if sclk:
             # the same fraction against the peak at the gfx clock measured while the kernel ran
             result["roofline"]["frac_at_sclk"] = tf / (PEAK_BF16_TFLOPS * sclk / 2400.0)
+        if zero_inputs:
+            result["roofline"]["zero_inputs"] = zero_inputs
     if "fp8" in ms:
         f = prefill_flops(2, 16, 8192, 128, True)
         tf = f / (ms["fp8"] * 1e-3) / 1e12
