@@ -23,7 +23,7 @@ __all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_quantize_fp8", "fa_fwd_bloc
            "fa_paged_decode", "fa_paged_decode_workspace_bytes", "fa_paged_decode_noalloc",
            "fa_noalloc_scratch_bytes", "fa_paged_prefill", "BlockManager",
            "fa_copy_pages",
-           "fa_status_str", "fa_version", "FaError"]
+           "fa_read_probe", "fa_status_str", "fa_version", "FaError"]
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -420,6 +420,18 @@ def fa_copy_pages(kcache: torch.Tensor, vcache: torch.Tensor, src: torch.Tensor,
     st = _lib.load().fa_copy_pages(_ptr(kcache), _ptr(vcache), _ptr(src), _ptr(dst), n, P, H, d, ps,
                                    _stream(kcache))
     _lib.check(st, "fa_copy_pages")
+
+
+@_on_device
+def fa_read_probe(src: torch.Tensor, sink: torch.Tensor) -> None:
+    """Stream-read every byte of the contiguous device tensor src once (a
+    measurement helper: the plain read rate of this GPU); XORs the data into
+    sink, a device int32 tensor of one element."""
+    if not isinstance(src, torch.Tensor) or src.device.type != "cuda" or not src.is_contiguous():
+        raise ValueError("src must be a contiguous device tensor")
+    _check_dev("sink", sink, torch.int32, (1,))
+    st = _lib.load().fa_read_probe(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(src))
+    _lib.check(st, "fa_read_probe")
 
 
 def fa_status_str(status: int) -> str:

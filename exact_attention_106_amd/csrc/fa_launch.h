@@ -57,6 +57,9 @@ inline size_t decode_workspace_bytes(int num_seqs, int H, int max_blocks_per_seq
            n_chunks * (sizeof(uint64_t) + 2 * sizeof(int)) + T * (sizeof(uint64_t) + sizeof(int)) + sizeof(int);
 }
 
+// Plain streaming read of bytes (a multiple of 16) at src; XOR of the data into *sink.
+hipError_t launch_read_probe(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream);
+
 hipError_t launch_fp8_quantize(const void *x, const void *rot, uint8_t *codes, float *scales, int B, int H,
                                int N, hipStream_t stream);
 

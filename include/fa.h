@@ -288,6 +288,18 @@ fa_status fa_bm_block_table(const void *state, int32_t *block_table, int32_t *ct
 fa_status fa_copy_pages(void *kcache, void *vcache, const int32_t *src, const int32_t *dst, int n,
                         int num_pages, int H, int d, int page_size, void *stream);
 
+/*
+ * Measurement helper, not part of the attention path: reads bytes (a
+ * multiple of 16, > 0) at the device pointer src once, as a plain streaming
+ * kernel, and XORs the data into the device word *sink (which the caller
+ * sets beforehand; its value only keeps the loads alive). Timed by the
+ * caller, it gives the HBM read rate a trivial kernel reaches on this GPU,
+ * the practical ceiling beside the spec peak for a kernel that only streams
+ * pages once (the paged decode). src 16-byte aligned, sink 4-byte aligned
+ * (FA_ERR_UNSUPPORTED otherwise).
+ */
+fa_status fa_read_probe(const void *src, size_t bytes, uint32_t *sink, void *stream);
+
 /* Human-readable name of a status (static string, never NULL). */
 const char *fa_status_str(fa_status s);
 
