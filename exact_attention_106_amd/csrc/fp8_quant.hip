@@ -175,8 +175,13 @@ __global__ __launch_bounds__(kQzThreads) void fp8_quant_kernel(const uint16_t *_
         for (int idx = tid; idx < kQzBlock * D / 16; idx += kQzThreads) {   // 16-byte pieces
             const int r = idx / (D / 16), c = idx % (D / 16);
             if (t0 + r < N)
-                *reinterpret_cast<u32x4 *>(codes + ((size_t)bh * N + t0 + r) * D + c * 16) =
-                    *reinterpret_cast<const u32x4 *>(sc + r * D + 16 * (c ^ ((r >> 1) & 7)));
+                // the codes are written once and not read back here: non-temporal
+                // stores (measured: 28.5 -> 23.6 us per tensor with R, 24.7 ->
+                // 20.1 us without; the same hint on the loads, whose 16-byte
+                // pieces of a line come from 8 different instructions, made
+                // them 40 % slower)
+                __builtin_nontemporal_store(*reinterpret_cast<const u32x4 *>(sc + r * D + 16 * (c ^ ((r >> 1) & 7))),
+                                            reinterpret_cast<u32x4 *>(codes + ((size_t)bh * N + t0 + r) * D + c * 16));
         }
         if (tid == 0) scales[item] = s;
     };
