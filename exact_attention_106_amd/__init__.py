@@ -129,7 +129,7 @@ def fa_fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, q_scale: to
                lse: Optional[torch.Tensor] = None, return_lse: bool = True
                ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """FP8 (E4M3FN) fused attention forward with fp32 scales per (b, h, 128-token block).
-    q8/k8/v8 uint8 or float8_e4m3fn [B, H, N, 128]; scales fp32 [B, H, ceil(N/128)]."""
+    q8/k8/v8 uint8 or float8_e4m3fn [B, H, N, d], d in {64, 128}; scales fp32 [B, H, ceil(N/128)]."""
     q8, k8, v8 = _as_u8("q8", q8), _as_u8("k8", k8), _as_u8("v8", v8)
     if q8.dim() != 4:
         raise ValueError("q8 must be [B, H, N, d]")

@@ -18,10 +18,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
-# the prefill kernel template (fwd_prefill.h) is instantiated in four units
+# the prefill kernel template (fwd_prefill.h) is instantiated in five units
 # that compile in parallel
 SOURCES = ["api.hip", "fwd_f32.hip", "fwd_prefill_bf16.hip", "fwd_prefill_bf16_d64.hip", "fwd_prefill_fp8.hip",
-           "fwd_prefill_paged.hip", "decode.hip", "bwd.hip", "block_manager.hip", "fwd_sparse.hip", "fp8_quant.hip",
+           "fwd_prefill_fp8_d64.hip", "fwd_prefill_paged.hip", "decode.hip", "bwd.hip", "block_manager.hip", "fwd_sparse.hip", "fp8_quant.hip",
            "read_probe.hip"]
 ARCH = "gfx950"
 
@@ -52,7 +52,8 @@ def common_flags():
 # slower, so that one keeps the default)
 PREFILL_FLAGS = ["-fno-honor-nans"]
 EXTRA = {"fwd_prefill_bf16.hip": PREFILL_FLAGS, "fwd_prefill_bf16_d64.hip": PREFILL_FLAGS,
-         "fwd_prefill_fp8.hip": PREFILL_FLAGS, "fwd_prefill_paged.hip": PREFILL_FLAGS,
+         "fwd_prefill_fp8.hip": PREFILL_FLAGS, "fwd_prefill_fp8_d64.hip": PREFILL_FLAGS,
+         "fwd_prefill_paged.hip": PREFILL_FLAGS,
          "bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
          "fwd_sparse.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 

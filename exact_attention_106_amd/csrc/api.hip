@@ -55,7 +55,7 @@ fa_status fa_fwd_fp8(const uint8_t *q8, const uint8_t *k8, const uint8_t *v8, co
     fa_status st = check_dense(q8, k8, v8, o, B, H, N, d, scale, causal);
     if (st != FA_OK) return st;
     if (!q_scale || !k_scale || !v_scale) return FA_ERR_NULL_PTR;
-    if (d != 128) return FA_ERR_UNSUPPORTED;
+    if (d != 128 && d != 64) return FA_ERR_UNSUPPORTED;
     return from_hip(fa::launch_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, H, N, d,
                                        scale, causal, static_cast<hipStream_t>(stream)));
 }

@@ -71,14 +71,18 @@ __device__ __forceinline__ void static_for(F &&f) {
 }
 
 // XOR swizzle of the 16-byte chunks of an LDS row of CPR chunks (CPR = 16:
-// 256-byte rows, CPR = 8: 128-byte rows): chunk c of row r is stored at
-// c ^ swz<CPR>(r). With it, 16-byte reads of one chunk column by 32 rows and
-// the 8-byte transpose reads (ds_read_b64_tr_b16) of 4 x 4 row-chunk blocks
-// are both free of bank conflicts.
+// 256-byte rows, CPR = 8: 128-byte rows, CPR = 4: 64-byte rows): chunk c of
+// row r is stored at c ^ swz<CPR>(r). With it, 16-byte reads of one chunk
+// column by 32 rows and the 8-byte transpose reads (ds_read_b64_tr_b16) of
+// 4 x 4 row-chunk blocks are both free of bank conflicts (64-byte rows carry
+// only 16-byte column reads: rows r and r + 4 share banks, the swizzle
+// moves them to different chunks).
 template <int CPR>
 __device__ __forceinline__ int swz(int r) {
+    static_assert(CPR == 16 || CPR == 8 || CPR == 4, "swizzle for 4, 8 or 16 chunks per row");
     if constexpr (CPR == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
-    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+    else if constexpr (CPR == 8) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+    else return (r >> 2) & 3;
 }
 
 // The running reference max of the online softmax only moves when a row's

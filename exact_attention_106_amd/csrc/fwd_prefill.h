@@ -1,6 +1,6 @@
 // Fused attention forward on gfx950 MFMA: bf16 (d = 64, 128) and FP8 E4M3
-// with per-block scales (d = 128), one kernel template for both. The
-// instantiations live in fwd_prefill_{bf16,bf16_d64,fp8,paged}.hip.
+// with per-block scales (d = 64, 128), one kernel template for both. The
+// instantiations live in fwd_prefill_{bf16,bf16_d64,fp8,fp8_d64,paged}.hip.
 //
 // Work decomposition (FlashAttention-2 parallelisation, 91haoming.cn article,
 // "FlashAttention v2 / parallelisation improvements"; "Flash Attention 再学习",
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
     uint16_t *__restrict__ O, float *__restrict__ LSE, int N, int BH, int n_rb, float c0, PagedArgs pg)
 {
     static_assert(!PAGED || (CAUSAL && !FP8 && D == 128), "paged: causal bf16, d = 128");
-    static_assert(!FP8 || D == 128, "fp8: d = 128 (the V chunk map covers 64 rows x 8 chunks with 2 loads per lane)");
+    static_assert(!FP8 || D == 128 || D == 64, "fp8: d = 64 or 128");
     using L = Layout3<D, FP8>;
     constexpr int KCPR = L::KROW / 16;
     constexpr int VCPR = L::VROW / 16;
@@ -454,12 +454,13 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
                   (uint32_t)(j * kBC) * L::KROW);
     };
     // fp8 V: 16-byte chunk idx = tid + 256 i of a tile is row v8_row(idx),
-    // chunk v8_chunk(idx) (16 E4M3 values). The 16 lanes of one LDS write pass
+    // chunk v8_chunk(idx) (16 E4M3 values; CH8 = D / 16 chunks per row). The 16 lanes of one LDS write pass
     // then hold 16 consecutive rows at one chunk, which the row swizzle spreads
     // over all banks (a row-major assignment puts 8 lanes of a pass on the even
     // chunks of one row and 8 on those of the next: two-way conflicts)
-    auto v8_row = [](int idx) { return (idx & 15) + 16 * (idx >> 7); };
-    auto v8_chunk = [](int idx) { return (idx >> 4) & 7; };
+    constexpr int CH8 = D / 16;
+    auto v8_row = [](int idx) { return (idx & 15) + 16 * (idx / (16 * CH8)); };
+    auto v8_chunk = [](int idx) { return (idx >> 4) % CH8; };
     auto v8_goff = [&](int i) {
         const int idx = tid + i * kThreads3;
         return (uint32_t)(v8_row(idx) * D + 16 * v8_chunk(idx));
@@ -829,7 +830,7 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
                     wait_vm_n<0>();
                     store_v8_part(j + 1, 0);
                 }
-                if constexpr (s == NS_PV + 2) store_v8_part(j + 1, 1);
+                if constexpr (L::V8_LOADS > 1 && s == NS_PV + 2) store_v8_part(j + 1, 1);
             }
             // 5. copies of this step: tile copies in the last slots, which
             // carry the least VALU work; fp8 V register loads in the first
@@ -1170,8 +1171,11 @@ hipError_t launch_t(const void *q, const void *k, const void *v, const float *qs
 
 }  // namespace
 
-// bf16 forward with d = 64 (its own translation unit, compiled in parallel)
+// bf16 and FP8 forward with d = 64 (their own translation units, compiled in parallel)
 hipError_t launch_fwd_bf16_d64(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
                                int N, float scale, int causal, hipStream_t stream);
+hipError_t launch_fwd_fp8_d64(const uint8_t *q8, const uint8_t *k8, const uint8_t *v8, const float *qs,
+                              const float *ks, const float *vs, void *o, float *lse, int B, int H, int N,
+                              float scale, int causal, hipStream_t stream);
 
 }  // namespace fa

@@ -79,7 +79,7 @@ fa_status fa_fwd_f32(const float *q, const float *k, const float *v, float *o, f
  * q8, k8, v8: OCP E4M3FN bytes [B, H, N, d]; q_scale, k_scale, v_scale: fp32
  * [B, H, ceil(N/128)], one per (batch, head, 128-token block); the value of an
  * element is decode(x8) * scale of its block. o: bf16 [B, H, N, d];
- * lse: fp32 [B, H, N] or NULL. d == 128. Codes are finite (no 0x7f / 0xff)
+ * lse: fp32 [B, H, N] or NULL. d in {64, 128}. Codes are finite (no 0x7f / 0xff)
  * and scales finite and >= 0; a q_scale, k_scale or v_scale entry below
  * 2^-100 (zero included) acts as 2^-100, which keeps the score multiplier
  * positive and moves O by far less than a bf16 ulp. Q.K^T runs on fp8 MFMA;

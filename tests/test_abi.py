@@ -81,7 +81,8 @@ def test_fp8_validation(lib):
     ok = dict(B=1, H=1, N=16, d=128)
     args = lambda qs=FAKE, d=128, N=16: (FAKE, FAKE, FAKE, qs, FAKE, FAKE, FAKE, None, 1, 1, N, d, 0.1, 1, None)
     assert f(*args(qs=None)) == NULL_PTR
-    assert f(*args(d=64)) == UNSUPPORTED
+    assert f(*args(d=96)) == UNSUPPORTED
+    assert f(*args(d=32)) == UNSUPPORTED
     assert f(*args(N=0)) == BAD_SHAPE
     assert ok
 

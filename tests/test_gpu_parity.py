@@ -197,6 +197,21 @@ def test_fp8_shapes(fa, gpu, N, causal):
     assert_close("fp8", f64_bf16(o), l.cpu().double().numpy(), ro, rl, 8e-2 + half_ulp_bf16(ro), 1e-3)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 17, 100, 300, 1000])
+def test_fp8_d64_shapes(fa, gpu, N, causal):
+    # d = 64: one 64-channel QK MFMA per key tile, 64-byte E4M3 K rows in LDS
+    # (their own swizzle) and one V register load per lane per tile
+    x = inputs.fp8_inputs(2, 2, N, 64, seed=700 + N, causal=causal)
+    log("fa_fwd_fp8 B2 H2 N%d d64 causal=%d" % (N, causal))
+    o, l = fa.fa_fwd_fp8(x.q8.to(gpu), x.k8.to(gpu), x.v8.to(gpu), x.q_scale.to(gpu),
+                         x.k_scale.to(gpu), x.v_scale.to(gpu), scale=x.scale, causal=causal)
+    torch.cuda.synchronize()
+    q, k, v = _fp8_ref(x)
+    ro, rl = oracle.attention(q, k, v, x.scale, causal)
+    assert_close("fp8 d64", f64_bf16(o), l.cpu().double().numpy(), ro, rl, 8e-2 + half_ulp_bf16(ro), 1e-3)
+
+
 def test_fp8_causal_B2H16N8192d128_sampled(fa, gpu):
     x = inputs.config4()
     log("fa_fwd_fp8 causal B2 H16 N8192 d128 (full size, sampled rows)")
