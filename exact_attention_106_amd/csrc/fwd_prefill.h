@@ -963,9 +963,17 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
             constexpr int f = decltype(fc)::value;
             if constexpr (f >= PRE && 2 * (f - PRE) >= NS) read(fc);
         });
+        // No LDS read of the block is in flight past its end. The compiler takes
+        // an asm result as ready at once; where blocks join (loop edges, the
+        // peeled first and last blocks) it may copy such a value or reuse the
+        // registers of one it thinks dead, and a read landing late would then
+        // be lost or overwrite them. The next step's barrier waits for these
+        // reads a few instructions later anyway.
+        wait_lgkm<0>();
         if constexpr (PREF) {
 #pragma unroll
             for (int p = 0; p < PRE; ++p) {
+                asm volatile("" : "+v"(nlo[p]), "+v"(nhi[p]));
                 pre_lo[p] = nlo[p];
                 pre_hi[p] = nhi[p];
             }

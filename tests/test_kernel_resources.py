@@ -4,7 +4,11 @@ LDS: no scratch (private memory), no vector-register spills, and LDS within the
 memory, and are allowed). Scratch in these kernels means register arrays indexed at run time or
 spills, which cost an order of magnitude in speed without changing results, so
 no numerical test would notice. Compiles each HIP source for the device only
-(same flags as the library build) and reads the compiler's resource remarks."""
+(same flags as the library build) and reads the compiler's resource remarks.
+
+The same assembly is checked for registers touched while a load into them is
+still in flight (isa_hazards): the kernels issue loads from inline asm, whose
+results the compiler takes as ready at once."""
 import concurrent.futures as cf
 import os
 import re
@@ -13,6 +17,7 @@ import tempfile
 
 import pytest
 
+import isa_hazards
 from exact_attention_106_amd import build as B
 
 LDS_LIMIT = 160 * 1024
@@ -21,9 +26,10 @@ LDS_LIMIT = 160 * 1024
 def remarks(src):
     with tempfile.TemporaryDirectory() as tmp:
         cmd = [B.hipcc()] + B.common_flags() + B.EXTRA.get(src, []) + [
-            "--offload-device-only", "-Rpass-analysis=kernel-resource-usage", "-c",
-            os.path.join(B.CSRC, src), "-o", os.path.join(tmp, "k.o")]
+            "--offload-device-only", "-Rpass-analysis=kernel-resource-usage", "-S",
+            os.path.join(B.CSRC, src), "-o", os.path.join(tmp, "k.s")]
         r = subprocess.run(cmd, capture_output=True, text=True)
+        asm = open(os.path.join(tmp, "k.s")).read() if r.returncode == 0 else ""
     assert r.returncode == 0, r.stderr[-2000:]
     kernels, cur = {}, None
     for line in r.stderr.splitlines():
@@ -35,7 +41,7 @@ def remarks(src):
         m = re.search(r"remark:\s+([A-Za-z ]+?)(?: \[bytes/(?:lane|block)\])?: (\d+)", line)
         if m and cur:
             kernels[cur][m.group(1).strip()] = int(m.group(2))
-    return kernels
+    return kernels, asm
 
 
 @pytest.fixture(scope="module")
@@ -46,9 +52,15 @@ def all_remarks():
 
 @pytest.mark.parametrize("src", [s for s in B.SOURCES if s != "api.hip"])
 def test_no_scratch_no_vgpr_spills(all_remarks, src):
-    kernels = all_remarks[src]
+    kernels = all_remarks[src][0]
     assert kernels, "no kernels found in %s" % src
     for name, k in kernels.items():
         assert k.get("ScratchSize", 0) == 0, (src, name, k)
         assert k.get("VGPRs Spill", 0) == 0, (src, name, k)
         assert k.get("LDS Size", 0) <= LDS_LIMIT, (src, name, k)
+
+
+@pytest.mark.parametrize("src", [s for s in B.SOURCES if s != "api.hip"])
+def test_no_register_touched_while_its_load_is_in_flight(all_remarks, src):
+    found = isa_hazards.hazards(all_remarks[src][1])
+    assert not found, "%s: %d accesses, first: %s" % (src, len(found), found[:3])
