@@ -183,10 +183,13 @@ def device_info(dev):
     return info
 
 
-def clock_window(fn, seconds=1.0):
+def clock_window(fn, seconds=2.0):
     """Run fn back to back for about `seconds` while another thread samples the
     current gfx clock of every XCD (amdsmi GPU metrics); returns the median
-    over samples of the mean XCD clock in MHz, or None without amdsmi."""
+    over the samples of the second half of the window of the mean XCD clock in
+    MHz, or None without amdsmi. The metrics table lags the activity (a window
+    right after a heavier one still reads that one's clock), so the first half
+    is not used."""
     import threading
     import torch
     try:
@@ -198,11 +201,12 @@ def clock_window(fn, seconds=1.0):
     samples, stop = [], threading.Event()
 
     def poll():
+        t_start = time.perf_counter()
         while not stop.is_set():
             try:
                 m = amdsmi.amdsmi_get_gpu_metrics_info(h)
                 clk = [c for c in m.get("current_gfxclks", []) if isinstance(c, (int, float)) and 0 < c < 10000]
-                if clk:
+                if clk and time.perf_counter() - t_start >= seconds / 2:
                     samples.append(sum(clk) / len(clk))
             except Exception:
                 pass
