@@ -37,11 +37,10 @@ struct Philox {
     uint32_t x[4];
 };
 
-// a ^ b ^ c in one instruction (the compiler emits two XORs here)
+// a ^ b ^ c in one instruction: the three-input bitwise op of gfx950 with
+// the truth table of XOR (0x96; the compiler emits two XORs here)
 __device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
-    uint32_t r;
-    asm("v_xor3_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "s"(c));
-    return r;
+    return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
 }
 
 // Philox4x32-10: ten rounds of two 32x32->64 multiplies with key bumps

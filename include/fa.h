@@ -291,8 +291,10 @@ fa_status fa_copy_pages(void *kcache, void *vcache, const int32_t *src, const in
 /*
  * Measurement helper, not part of the attention path: reads bytes (a
  * multiple of 16, > 0) at the device pointer src once, as a plain streaming
- * kernel, and XORs the data into the device word *sink (which the caller
- * sets beforehand; its value only keeps the loads alive). Timed by the
+ * kernel (one contiguous slab per workgroup), and XORs every 32-bit word it
+ * read into the device word *sink (which the caller sets beforehand; the
+ * result only keeps the loads alive, and shows that each word was read once
+ * when checked against the host). Timed by the
  * caller, it gives the HBM read rate a trivial kernel reaches on this GPU,
  * the practical ceiling beside the spec peak for a kernel that only streams
  * pages once (the paged decode). src 16-byte aligned, sink 4-byte aligned

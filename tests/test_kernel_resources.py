@@ -24,21 +24,26 @@ LDS_LIMIT = 160 * 1024
 
 
 def remarks(src):
+    # compiled to an object (so the assembler checks every instruction, inline
+    # asm included) with the intermediate assembly kept for the scan
     with tempfile.TemporaryDirectory() as tmp:
         cmd = [B.hipcc()] + B.common_flags() + B.EXTRA.get(src, []) + [
-            "--offload-device-only", "-Rpass-analysis=kernel-resource-usage", "-S",
-            os.path.join(B.CSRC, src), "-o", os.path.join(tmp, "k.s")]
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        asm = open(os.path.join(tmp, "k.s")).read() if r.returncode == 0 else ""
+            "--offload-device-only", "-Rpass-analysis=kernel-resource-usage", "-c", "--save-temps",
+            os.path.join(B.CSRC, src), "-o", os.path.join(tmp, "k.o")]
+        r = subprocess.run(cmd, capture_output=True, text=True, cwd=tmp)
+        s_files = [f for f in os.listdir(tmp) if f.endswith("gfx950.s")]
+        asm = open(os.path.join(tmp, s_files[0])).read() if r.returncode == 0 and s_files else ""
     assert r.returncode == 0, r.stderr[-2000:]
+    assert asm, "no gfx950 assembly for %s" % src
     kernels, cur = {}, None
     for line in r.stderr.splitlines():
-        m = re.search(r"remark: Function Name: (\S+)", line)
+        # "<file>: remark: <text>" or, with --save-temps, "remark: <file>: <text>"
+        m = re.search(r"remark:.*?Function Name: (\S+)", line)
         if m:
             cur = m.group(1)
             kernels[cur] = {}
             continue
-        m = re.search(r"remark:\s+([A-Za-z ]+?)(?: \[bytes/(?:lane|block)\])?: (\d+)", line)
+        m = re.search(r"remark:.*?:\s+([A-Za-z ]+?)(?: \[bytes/(?:lane|block)\])?: (\d+) \[-Rpass", line)
         if m and cur:
             kernels[cur][m.group(1).strip()] = int(m.group(2))
     return kernels, asm
