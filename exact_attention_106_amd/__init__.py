@@ -12,14 +12,14 @@ from __future__ import annotations
 import ctypes
 import functools
 import math
-from typing import Optional, Tuple
+from typing import Optional, Sequence, Tuple
 
 import torch
 
 from . import _lib
 from ._lib import FaError
 
-__all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_quantize_fp8", "fa_fwd_block_sparse", "fa_bwd", "fa_bwd_workspace_bytes",
+__all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_quantize_fp8", "fa_quantize_fp8_qkv", "fa_fwd_block_sparse", "fa_bwd", "fa_bwd_workspace_bytes",
            "fa_paged_decode", "fa_paged_decode_workspace_bytes", "fa_paged_decode_noalloc",
            "fa_noalloc_scratch_bytes", "fa_paged_prefill", "BlockManager",
            "fa_copy_pages",
@@ -180,6 +180,42 @@ def fa_quantize_fp8(x: torch.Tensor, rot: Optional[torch.Tensor] = None,
     st = _lib.load().fa_quantize_fp8(_ptr(x), _ptr(rot), _ptr(codes), _ptr(scales), B, H, N, d, _stream(x))
     _lib.check(st, "fa_quantize_fp8")
     return codes, scales
+
+
+@_on_device
+def fa_quantize_fp8_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rot: Optional[torch.Tensor] = None,
+                        out: Optional[Sequence[Tuple[torch.Tensor, torch.Tensor]]] = None
+                        ) -> Tuple[Tuple[torch.Tensor, torch.Tensor], ...]:
+    """fa_fwd_fp8's three inputs in one launch: Q and K rotated by rot (or not, if
+    None), V never, each quantised as fa_quantize_fp8 does. Returns ((q_codes,
+    q_scales), (k_codes, k_scales), (v_codes, v_scales)); out, if given, is that
+    tuple of preallocated tensors."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(name, t, torch.bfloat16)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    _check_dev("k", k, torch.bfloat16, (B, H, N, d))
+    _check_dev("v", v, torch.bfloat16, (B, H, N, d))
+    if rot is not None:
+        _check_dev("rot", rot, torch.bfloat16, (d, d))
+    nsb = (N + 127) // 128
+    if out is None:
+        out = [(torch.empty((B, H, N, d), dtype=torch.uint8, device=q.device),
+                torch.empty((B, H, nsb), dtype=torch.float32, device=q.device)) for _ in range(3)]
+    if len(out) != 3:
+        raise ValueError("out must hold three (codes, scales) pairs")
+    res = []
+    for name, (c, sc) in zip("qkv", out):
+        c = _as_u8(name + "_codes", c)
+        _check_dev(name + "_codes", c, torch.uint8, (B, H, N, d))
+        _check_dev(name + "_scales", sc, torch.float32, (B, H, nsb))
+        res.append((c, sc))
+    (qc, qs), (kc, ks), (vc, vs) = res
+    st = _lib.load().fa_quantize_fp8_qkv(_ptr(q), _ptr(k), _ptr(v), _ptr(rot), _ptr(qc), _ptr(kc), _ptr(vc),
+                                         _ptr(qs), _ptr(ks), _ptr(vs), B, H, N, d, _stream(q))
+    _lib.check(st, "fa_quantize_fp8_qkv")
+    return tuple(res)
 
 
 @_on_device

@@ -15,7 +15,8 @@ STATUS_NAMES = {
     8: "FA_ERR_SCRATCH_LIMIT",
 }
 # every symbol include/fa.h declares
-EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_quantize_fp8", "fa_fwd_block_sparse", "fa_bwd_workspace_bytes", "fa_bwd",
+EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_quantize_fp8", "fa_quantize_fp8_qkv",
+           "fa_fwd_block_sparse", "fa_bwd_workspace_bytes", "fa_bwd",
            "fa_paged_decode_workspace_bytes", "fa_paged_decode", "fa_noalloc_scratch_bytes",
            "fa_paged_decode_noalloc", "fa_paged_prefill",
            "fa_bm_state_bytes", "fa_bm_init",
@@ -64,6 +65,8 @@ def load() -> ctypes.CDLL:
         lib.fa_paged_decode_noalloc.restype = i
         lib.fa_quantize_fp8.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
         lib.fa_quantize_fp8.restype = i
+        lib.fa_quantize_fp8_qkv.argtypes = [vp] * 10 + [i, i, i, i, vp]
+        lib.fa_quantize_fp8_qkv.restype = i
         lib.fa_fwd_block_sparse.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, f, ctypes.c_uint64, vp]
         lib.fa_fwd_block_sparse.restype = i
         lib.fa_paged_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]

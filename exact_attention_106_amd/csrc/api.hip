@@ -73,6 +73,26 @@ fa_status fa_quantize_fp8(const void *x, const void *rot, uint8_t *codes, float 
     return from_hip(fa::launch_fp8_quantize(x, rot, codes, scales, B, H, N, static_cast<hipStream_t>(stream)));
 }
 
+fa_status fa_quantize_fp8_qkv(const void *q, const void *k, const void *v, const void *rot, uint8_t *q_codes,
+                              uint8_t *k_codes, uint8_t *v_codes, float *q_scales, float *k_scales, float *v_scales,
+                              int B, int H, int N, int d, void *stream)
+{
+    if (!q || !k || !v || !q_codes || !k_codes || !v_codes || !q_scales || !k_scales || !v_scales)
+        return FA_ERR_NULL_PTR;
+    if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return FA_ERR_BAD_SHAPE;
+    if ((long long)B * H * N * d > kMaxElems) return FA_ERR_BAD_SHAPE;
+    if (d != 128) return FA_ERR_UNSUPPORTED;
+    const uintptr_t mis = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+                          reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(rot) |
+                          reinterpret_cast<uintptr_t>(q_codes) | reinterpret_cast<uintptr_t>(k_codes) |
+                          reinterpret_cast<uintptr_t>(v_codes);
+    const uintptr_t mis_s = reinterpret_cast<uintptr_t>(q_scales) | reinterpret_cast<uintptr_t>(k_scales) |
+                            reinterpret_cast<uintptr_t>(v_scales);
+    if ((mis & 15) || (mis_s & 3)) return FA_ERR_UNSUPPORTED;
+    return from_hip(fa::launch_fp8_quantize_qkv(q, k, v, rot, q_codes, k_codes, v_codes, q_scales, k_scales,
+                                                v_scales, B, H, N, static_cast<hipStream_t>(stream)));
+}
+
 fa_status fa_fwd_block_sparse(const void *q, const void *k, const void *v, const uint8_t *block_mask,
                               void *o, float *lse, int B, int H, int N, int d, float scale, int causal,
                               float dropout_p, uint64_t seed, void *stream)

@@ -62,6 +62,10 @@ hipError_t launch_read_probe(const void *src, size_t bytes, uint32_t *sink, hipS
 
 hipError_t launch_fp8_quantize(const void *x, const void *rot, uint8_t *codes, float *scales, int B, int H,
                                int N, hipStream_t stream);
+// The same for Q, K (rotated when rot is given) and V (never rotated) in one launch.
+hipError_t launch_fp8_quantize_qkv(const void *q, const void *k, const void *v, const void *rot, uint8_t *q_codes,
+                                   uint8_t *k_codes, uint8_t *v_codes, float *q_scales, float *k_scales,
+                                   float *v_scales, int B, int H, int N, hipStream_t stream);
 
 hipError_t launch_fwd_block_sparse(const void *q, const void *k, const void *v, const uint8_t *block_mask,
                                    void *o, float *lse, int B, int H, int N, float scale, int causal,

@@ -111,6 +111,24 @@ fa_status fa_quantize_fp8(const void *x, const void *rot, uint8_t *codes, float 
                           int N, int d, void *stream);
 
 /*
+ * The three inputs of fa_fwd_fp8 in one launch: Q and K multiplied by rot
+ * (the one R that leaves QK^T unchanged; NULL for no rotation), V not
+ * rotated, each block-quantised as fa_quantize_fp8 does (same pages). The
+ * codes and scales are bit for bit those of three fa_quantize_fp8 calls
+ * (q with rot, k with rot, v with NULL); one grid covers all three, so the
+ * start and tail of two launches are saved.
+ *   q, k, v: bf16 [B, H, N, d], device; rot: bf16 [d, d] or NULL;
+ *   q_codes, k_codes, v_codes: uint8 [B, H, N, d]; q_scales, k_scales,
+ *   v_scales: fp32 [B, H, ceil(N/128)]. Outputs must not overlap the inputs
+ *   or each other.
+ * Errors and requirements as for fa_quantize_fp8 (FA_ERR_NULL_PTR for any
+ * NULL pointer other than rot). Asynchronous on stream.
+ */
+fa_status fa_quantize_fp8_qkv(const void *q, const void *k, const void *v, const void *rot, uint8_t *q_codes,
+                              uint8_t *k_codes, uint8_t *v_codes, float *q_scales, float *k_scales,
+                              float *v_scales, int B, int H, int N, int d, void *stream);
+
+/*
  * Block-sparse attention forward with optional dropout, bf16 (d == 128).
  * Block-sparse FlashAttention (91haoming.cn FlashAttention v1-v3 article, v1
  * results): the fused tile loop runs only over the (query block, key block)

@@ -152,6 +152,27 @@ def test_quantize_validation(lib):
     assert call(s=FAKE + 2) == UNSUPPORTED
 
 
+def test_quantize_qkv_validation(lib):
+    f = lib.fa_quantize_fp8_qkv
+    names = ("q", "k", "v", "r", "qc", "kc", "vc", "qs", "ks", "vs")
+
+    def call(B=1, H=1, N=16, d=128, **kw):
+        ptrs = [kw.get(n, None if n == "r" else FAKE) for n in names]
+        return f(*ptrs, B, H, N, d, None)
+    for n in names:
+        if n != "r":
+            assert call(**{n: None}) == NULL_PTR, n
+    assert call(N=0) == BAD_SHAPE
+    assert call(H=-1) == BAD_SHAPE
+    assert call(B=1 << 12, H=1 << 12, N=1 << 10) == BAD_SHAPE
+    assert call(d=64) == UNSUPPORTED
+    for n in ("q", "k", "v", "qc", "kc", "vc"):
+        assert call(**{n: FAKE + 8}) == UNSUPPORTED, n   # 16-byte alignment
+    assert call(r=FAKE + 2) == UNSUPPORTED
+    for n in ("qs", "ks", "vs"):
+        assert call(**{n: FAKE + 2}) == UNSUPPORTED, n
+
+
 def test_paged_decode_noalloc_validation(lib):
     # the static workspace bounds the sizes: 80 MiB per device
     limit = lib.fa_noalloc_scratch_bytes()

@@ -103,6 +103,26 @@ def test_quantize_zero_block_and_reuse(gpu):
     check("quant zero block", x, r, codes, scales)
 
 
+def test_quantize_negative_zeros(gpu):
+    """-0 inputs without a rotation: scattered through an ordinary block and
+    filling a whole block (scale 1). E4M3 has a signed zero, so their code is
+    0x80, in fa_quantize_fp8 and as the V of fa_quantize_fp8_qkv."""
+    x, r = inputs.quant_inputs(1, 2, 300, 128, seed=1210)
+    xf = x.float()
+    xf[:, :, :128, ::7] = -0.0
+    xf[:, 1, 128:256] = -0.0
+    xs = xf.to(torch.bfloat16)
+    assert int((xs.view(torch.int16) == -32768).sum()) > 128 * 128
+    log("fa_quantize_fp8 B1 H2 N300 with -0 inputs, no rotation")
+    codes, scales = fa.fa_quantize_fp8(xs.to(gpu), None)
+    (_, _), (_, _), (vc, vs) = fa.fa_quantize_fp8_qkv(x.to(gpu), x.to(gpu), xs.to(gpu), r.to(gpu))
+    torch.cuda.synchronize()
+    assert int(codes[0, 1, 128:256].min()) == 0x80 and int(codes[0, 1, 128:256].max()) == 0x80
+    assert float(scales[0, 1, 1]) == 1.0
+    assert torch.equal(codes, vc) and torch.equal(scales, vs)
+    check("quant -0", xs, None, codes, scales)
+
+
 def test_quantize_extreme_block_scales(gpu):
     """Blocks with scales far below and far above ordinary data (x times 2^-100
     and 2^110, exact in bf16) next to an ordinary block, with and without R: the
@@ -132,6 +152,44 @@ def test_quantize_full_size_B2H16N8192(gpu):
         codes, scales = fa.fa_quantize_fp8(x.to(gpu), r.to(gpu) if rot else None)
         torch.cuda.synchronize()
         check("quant full %d" % i, x, r if rot else None, codes, scales)
+
+
+def _qkv(B, H, N, seed):
+    (q, r), (k, _), (v, _) = [inputs.quant_inputs(B, H, N, 128, seed=seed + i) for i in range(3)]
+    return q, k, v, r
+
+
+@pytest.mark.parametrize("B,H,N,rot", [(1, 1, 1, True), (1, 2, 300, True), (1, 2, 300, False),
+                                       (2, 3, 777, True), (2, 8, 8200, True), (1, 3, 4000, False)])
+def test_quantize_qkv_matches_oracle_and_single_calls(gpu, B, H, N, rot):
+    """The one-launch Q/K/V quantiser: every output against the oracle (Q and K
+    rotated, V not), and bit for bit the codes and scales of three
+    fa_quantize_fp8 calls. The shapes give grids below and above the
+    persistent grid (B2 H8 N8200: 3120 items) and short last blocks."""
+    q, k, v, r = _qkv(B, H, N, 1500 + N)
+    rr = r if rot else None
+    log("fa_quantize_fp8_qkv B%d H%d N%d rot=%d" % (B, H, N, rot))
+    got = fa.fa_quantize_fp8_qkv(q.to(gpu), k.to(gpu), v.to(gpu), rr.to(gpu) if rot else None)
+    one = [fa.fa_quantize_fp8(t.to(gpu), rt.to(gpu) if rt is not None else None)
+           for t, rt in ((q, rr), (k, rr), (v, None))]
+    torch.cuda.synchronize()
+    for name, t, rt, (c, s), (c1, s1) in zip("qkv", (q, k, v), (rr, rr, None), got, one):
+        assert torch.equal(c, c1) and torch.equal(s, s1), name + ": differs from fa_quantize_fp8"
+        check("qkv %s B%dH%dN%d r%d" % (name, B, H, N, rot), t, rt, c, s)
+
+
+def test_quantize_qkv_full_size_B2H16N8192(gpu):
+    """The launch the benchmark times, on its inputs (seeds 40, 41, 42), into
+    preallocated outputs holding stale bytes, compared in full."""
+    q, k, v, r = _qkv(2, 16, 8192, 40)
+    out = [(torch.full((2, 16, 8192, 128), 0x7f, dtype=torch.uint8, device=gpu),
+            torch.full((2, 16, 64), float("nan"), dtype=torch.float32, device=gpu)) for _ in range(3)]
+    log("fa_quantize_fp8_qkv B2 H16 N8192 d128 (full size)")
+    got = fa.fa_quantize_fp8_qkv(q.to(gpu), k.to(gpu), v.to(gpu), r.to(gpu), out=out)
+    torch.cuda.synchronize()
+    for name, t, rt, (c, s), (c0, s0) in zip("qkv", (q, k, v), (r, r, None), got, out):
+        assert c.data_ptr() == c0.data_ptr() and s.data_ptr() == s0.data_ptr()
+        check("qkv full %s" % name, t, rt, c, s)
 
 
 def test_quantize_then_fp8_attention(gpu):

@@ -69,3 +69,17 @@ def test_no_scratch_no_vgpr_spills(all_remarks, src):
 def test_no_register_touched_while_its_load_is_in_flight(all_remarks, src):
     found = isa_hazards.hazards(all_remarks[src][1])
     assert not found, "%s: %d accesses, first: %s" % (src, len(found), found[:3])
+
+
+def test_quantiser_fits_three_workgroups_per_cu(all_remarks):
+    """The quantiser's grid is three persistent workgroups of four waves per CU:
+    every instantiation (plain, rotated, and the mixed Q/K/V launch) must fit
+    three waves per SIMD, 512 / 3 -> at most 168 registers per lane, and three
+    workgroups' LDS."""
+    kernels = all_remarks["fp8_quant.hip"][0]
+    assert len(kernels) == 3, sorted(kernels)
+    for name, k in kernels.items():
+        vg = (k.get("VGPRs", 0) + 7) // 8 * 8
+        regs = vg + k.get("AGPRs", 0) if k.get("AGPRs", 0) else vg
+        assert regs <= 168, (name, k)
+        assert 3 * k.get("LDS Size", 0) <= 160 * 1024, (name, k)
