@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kQzThreads) __attribute__((amdgpu_waves_per_eu(3)))
 {
     constexpr int D = 128, ROW = 2 * D, CPR = D / 8, KC = D / 16, NT = D / 32;
     __shared__ __attribute__((aligned(16))) uint8_t sc[kQzBlock * D];  // codes of one block
-    __shared__ float wmax[4];
+    __shared__ float wmax[2][4];   // per-wave maxima, double-buffered by item parity
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, h = lane >> 5;
     const int tl = 32 * w + l32;   // token of the lane within the block
@@ -116,8 +116,9 @@ __global__ __launch_bounds__(kQzThreads) __attribute__((amdgpu_waves_per_eu(3)))
     // M = 0: a plain item; 1: a rotated item; 2: decided per item (jobs
     // [0, nrot) rotated), with one body for both kinds so that the mixed
     // kernel needs no more registers than the rotated one.
-    auto process_as = [&](int item, const u32x4 (&xb)[KC], auto modec) __attribute__((always_inline)) {
+    auto process_as = [&](int item, const u32x4 (&xb)[KC], auto modec, auto parc) __attribute__((always_inline)) {
         constexpr int M = decltype(modec)::value;
+        constexpr int PAR = decltype(parc)::value;   // parity of the item in this workgroup's sequence
         const int j = item / per, loc = item - j * per;
         uint8_t *const codes = pick3(jobs.codes, j);
         const bool rot_item = M == 1 || (M == 2 && item < nrot * per);
@@ -162,9 +163,12 @@ __global__ __launch_bounds__(kQzThreads) __attribute__((amdgpu_waves_per_eu(3)))
         }
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-        if (lane == 0) wmax[w] = amax;
-        lds_barrier();   // LDS only: the next item's loads stay in flight
-        const float bmax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+        // The one barrier per item (LDS only: the next item's loads stay in
+        // flight). A wave writes wmax[PAR] again only two items later, after
+        // the next item's barrier, which every wave reaches after reading it.
+        if (lane == 0) wmax[PAR][w] = amax;
+        lds_barrier();
+        const float bmax = fmaxf(fmaxf(wmax[PAR][0], wmax[PAR][1]), fmaxf(wmax[PAR][2], wmax[PAR][3]));
         const float s = bmax > 0.f ? bmax / 448.f : 1.f;
         // y / s rounded correctly to fp32. For 2^-80 <= s <= 2^100 (every
         // block of ordinary data) it is refined from q0 = y * RN(1/s) with two
@@ -227,35 +231,38 @@ __global__ __launch_bounds__(kQzThreads) __attribute__((amdgpu_waves_per_eu(3)))
         };
         if (refine) emit(std::true_type{});
         else emit(std::false_type{});
-        lds_barrier();
-        // the codes are written once and not read back here: non-temporal
-        // stores (measured: 28.5 -> 23.6 us per tensor with R, 24.7 -> 20.1 us
-        // without; the same hint on the loads, whose 16-byte pieces of a line
-        // come from 8 different instructions, made them 40 % slower)
+        // Each wave stores the rows of its own 32 tokens (4 KiB, contiguous in
+        // memory), which it staged itself: its LDS writes and reads complete in
+        // issue order, so no barrier is needed between them, and the staging
+        // rows are rewritten only by the same wave's next item. The codes are
+        // written once and not read back here: non-temporal stores (measured:
+        // 28.5 -> 23.6 us per tensor with R, 24.7 -> 20.1 us without; the same
+        // hint on the loads, whose 16-byte pieces of a line come from 8
+        // different instructions, made them 40 % slower).
         const __amdgpu_buffer_rsrc_t cs =
             __builtin_amdgcn_make_buffer_rsrc((void *)(codes + block_off(loc)), 0, rows_of(loc) * D, kRsrcFlags);
 #pragma unroll
-        for (int i = 0; i < kQzBlock * D / 16 / kQzThreads; ++i) {   // 16-byte pieces
-            const int idx = tid + i * kQzThreads, r = idx / (D / 16), c = idx % (D / 16);
+        for (int i = 0; i < 32 * D / 16 / 64; ++i) {   // 16-byte pieces of the wave's rows
+            const int idx = lane + 64 * i, r = 32 * w + idx / (D / 16), c = idx % (D / 16);
             __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4 *>(sc + r * D + 16 * (c ^ ((r >> 1) & 7))),
-                                                   cs, 16 * idx, 0, kNonTemporal);
+                                                   cs, 16 * (32 * w * (D / 16) + idx), 0, kNonTemporal);
         }
         // one scale per item, from thread 0 (the descriptor holds 4 bytes)
         const __amdgpu_buffer_rsrc_t ss =
             __builtin_amdgcn_make_buffer_rsrc((void *)(pick3(jobs.scales, j) + loc), 0, 4, kRsrcFlags);
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s), ss, 4 * tid, 0, 0);
     };
-    auto process = [&](int item, const u32x4 (&xb)[KC]) __attribute__((always_inline)) {
-        process_as(item, xb, std::integral_constant<int, !ROT ? 0 : MIXED ? 2 : 1>{});
+    auto process = [&](int item, const u32x4 (&xb)[KC], auto parc) __attribute__((always_inline)) {
+        process_as(item, xb, std::integral_constant<int, !ROT ? 0 : MIXED ? 2 : 1>{}, parc);
     };
     u32x4 xa[KC], xc[KC];
     load_item(blockIdx.x, xa);
     for (int item = blockIdx.x; item < total; item += 2 * (int)gridDim.x) {
         load_item(item + gridDim.x, xc);
-        process(item, xa);
+        process(item, xa, std::integral_constant<int, 0>{});
         if (item + (int)gridDim.x >= total) break;
         load_item(item + 2 * gridDim.x, xa);
-        process(item + gridDim.x, xc);
+        process(item + gridDim.x, xc, std::integral_constant<int, 1>{});
     }
 }
 
