@@ -2,18 +2,19 @@
 
 One step = one pass of the whole path over resident synthetic inputs:
   1. fa_fwd      bf16 causal prefill, B=1 H=32 N=16384 d=128   (headline)
-  2. fa_fwd_fp8  E4M3 causal prefill, B=2 H=16 N=8192 d=128
-  3. fa_paged_decode  64 sequences, H=32, d=128, contexts 512..32768
-  4. fa_bwd      backward of (1) given its O, L and a seeded dO (the first
+  2. fa_quantize_fp8_qkv  rotation + E4M3 block quantiser of Q, K (with R)
+                 and V (without) of the fp8 workload's shape, one launch,
+                 timed before the fp8 forward as a caller runs them
+  3. fa_fwd_fp8  E4M3 causal prefill, B=2 H=16 N=8192 d=128
+  4. fa_paged_decode  64 sequences, H=32, d=128, contexts 512..32768
+  5. fa_bwd      backward of (1) given its O, L and a seeded dO (the first
                  of the next rows; TFLOP/s on the 5-product count, 2.5x the
                  forward's)
-  5. fa_paged_prefill  chunked prefill through the block table: the last
+  6. fa_paged_prefill  chunked prefill through the block table: the last
                  2048 tokens of 16 sequences (contexts 2048..16384), H=32, d=128
-  6. fa_fwd_block_sparse  the inputs of (1) with a seeded block mask keeping
+  7. fa_fwd_block_sparse  the inputs of (1) with a seeded block mask keeping
                  half of the causal 128 x 128 blocks (the diagonal always),
                  without and with dropout p = 0.1
-  7. fa_quantize_fp8_qkv  rotation + E4M3 block quantiser of the fp8
-                 workload's Q, K (with R) and V (without), one launch
   8. fa_fwd      bf16 non-causal MHA, B=4 H=16 N=2048 d=64
 Each launch is bracketed by HIP events on the stream it runs on. `value` is
 the prefill's TFLOP/s (4*B*H*N^2*d, halved for causal, per the kernel's mean
@@ -329,6 +330,16 @@ def main():
         o3 = torch.empty_like(q3)
         l3 = torch.empty(q3.shape[:3], dtype=torch.float32, device=dev)
         parts.append(("prefill", lambda: fa.fa_fwd(q3, k3, v3, scale=x3.scale, causal=True, out=o3, lse=l3)))
+    if "fp8_quantize" in only:
+        # Q and K of the fp8 workload's shape with the incoherent rotation, V
+        # without; timed right before the FP8 forward, the order a caller runs them
+        qz = [inputs.quant_inputs(2, 16, 8192, 128, seed=40 + i) for i in range(3)]
+        digests["fp8_quantize_B2H16N8192d128"] = digest(*[x for x, _ in qz], qz[0][1])
+        xz = [x.to(dev) for x, _ in qz]
+        rz = qz[0][1].to(dev)
+        oz = [(torch.empty(x.shape, dtype=torch.uint8, device=dev),
+               torch.empty((2, 16, 64), dtype=torch.float32, device=dev)) for x in xz]
+        parts.append(("fp8_quantize", lambda: fa.fa_quantize_fp8_qkv(*xz, rz, out=oz)))
     if "fp8" in only:
         x4 = inputs.config4()
         digests["causal_fp8_B2H16N8192d128"] = digest(x4.q8, x4.k8, x4.v8, x4.q_scale, x4.k_scale, x4.v_scale)
@@ -377,14 +388,6 @@ def main():
         parts.append(("block_sparse_dropout", lambda: fa.fa_fwd_block_sparse(q3, k3, v3, bmask_d, scale=x3.scale,
                                                                              causal=True, dropout_p=0.1, seed=11,
                                                                              out=o7, lse=l7)))
-    if "fp8_quantize" in only:
-        # Q and K of the fp8 workload with the incoherent rotation, V without
-        qz = [inputs.quant_inputs(2, 16, 8192, 128, seed=40 + i) for i in range(3)]
-        xz = [x.to(dev) for x, _ in qz]
-        rz = qz[0][1].to(dev)
-        oz = [(torch.empty(x.shape, dtype=torch.uint8, device=dev),
-               torch.empty((2, 16, 64), dtype=torch.float32, device=dev)) for x in xz]
-        parts.append(("fp8_quantize", lambda: fa.fa_quantize_fp8_qkv(*xz, rz, out=oz)))
     if "mha" in only:
         x2 = inputs.config2()
         digests["mha_bf16_B4H16N2048d64"] = digest(x2.q, x2.k, x2.v)
