@@ -61,15 +61,20 @@ __device__ __forceinline__ Philox philox4x32_10(uint32_t c0, uint32_t c1, uint32
     return Philox{{c0, c1, c2, c3}};
 }
 
+// Without dropout two workgroups share a CU (2 waves per SIMD, 256 registers,
+// a two-stage ring in 68 KiB of LDS): one workgroup's softmax runs while the
+// other's MFMAs do, which a single wave's order (S, softmax, P V) does not
+// allow. Dropout's generator needs more registers than that: one workgroup per
+// CU, a three-stage ring, copies two tiles ahead.
 template <bool CAUSAL, bool DROPOUT>
-__global__ __launch_bounds__(kSpThreads, 1) void sparse_fwd_kernel(
+__global__ __launch_bounds__(kSpThreads) __attribute__((amdgpu_waves_per_eu(DROPOUT ? 1 : 2, DROPOUT ? 1 : 2))) void sparse_fwd_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     const uint8_t *__restrict__ MASK, uint16_t *__restrict__ O, float *__restrict__ LSE, int N, int BH,
     int n_qb, float scale, uint32_t drop_threshold, float inv_keep, uint32_t seed_lo, uint32_t seed_hi)
 {
     constexpr int D = 128, ROW = 2 * D, CPR = D / 8, KC = D / 16, DT = D / 32;
     constexpr int TILE = kSpTile * ROW;
-    constexpr int STAGES = 3;
+    constexpr int STAGES = DROPOUT ? 3 : 2;
     constexpr int NDMA = TILE / 1024 / 4;          // 1 KiB copies per wave and tensor
     __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * 2 * TILE];
     __shared__ int16_t tiles[kSpMaxTiles];
@@ -154,7 +159,7 @@ __global__ __launch_bounds__(kSpThreads, 1) void sparse_fwd_kernel(
     float m = neg_inf(), lsum = 0.f;
     const float c = scale * kLog2e;
 
-    constexpr int NSD = 2 * KC, NST = NSD + 4 * DT, LA = 4;
+    constexpr int NSD = 2 * KC, NST = NSD + 4 * DT, LA = DROPOUT ? 4 : 3;
     auto tile = [&](int kt, auto sc, auto mc) __attribute__((always_inline)) {
         constexpr int S = decltype(sc)::value;
         constexpr bool MASKED = decltype(mc)::value;
@@ -243,35 +248,57 @@ __global__ __launch_bounds__(kSpThreads, 1) void sparse_fwd_kernel(
     // List entry u uses LDS stage u mod 3; its step issues the copies of
     // entry u + 2 and ends once entry u + 1 is in LDS. A tile needs the mask
     // when it reaches past N or (causal) past the wave's first query.
+    // Two stages: entry u uses stage u mod 2; its step issues the copies of
+    // entry u + 1 into the other stage (free since the last barrier) and ends
+    // once they have landed. Three stages: entry u uses stage u mod 3; its
+    // step issues entry u + 2 and ends once entry u + 1 is in LDS. A tile
+    // needs the mask when it reaches past N or (causal) past the wave's first
+    // query.
+    constexpr int AHEAD = STAGES - 1;
     auto step = [&](int u, auto sc) __attribute__((always_inline)) {
         constexpr int S = decltype(sc)::value;
-        const bool ahead = u + 2 < n_kt;
-        if (ahead) issue(u + 2, (S + 2) % STAGES);
+        const bool ahead = u + AHEAD < n_kt;
+        if (ahead) issue(u + AHEAD, (S + AHEAD) % STAGES);
         const int kt = __builtin_amdgcn_readfirstlane((int)tiles[u]);
         const int last_key = kt * kSpTile + kSpTile - 1;
         if (last_key >= N || (CAUSAL && last_key > qw)) tile(kt, sc, std::true_type{});
         else tile(kt, sc, std::false_type{});
-        if (ahead) wait_vm_n<2 * NDMA>();
+        if (AHEAD == 2 && ahead) wait_vm_n<2 * NDMA>();
         else wait_vm_n<0>();
         __syncthreads();
     };
+    using St0 = std::integral_constant<int, 0>;
+    using St1 = std::integral_constant<int, 1>;
+    using St2 = std::integral_constant<int, 2>;
     if (n_kt > 0) {
         issue(0, 0);
-        if (1 < n_kt) {
-            issue(1, 1);
-            wait_vm_n<2 * NDMA>();
+        if constexpr (STAGES == 3) {
+            if (1 < n_kt) {
+                issue(1, 1);
+                wait_vm_n<2 * NDMA>();
+            } else {
+                wait_vm_n<0>();
+            }
         } else {
             wait_vm_n<0>();
         }
         __syncthreads();
         int u = 0;
-        for (; u + 2 < n_kt; u += 3) {
-            step(u, std::integral_constant<int, 0>{});
-            step(u + 1, std::integral_constant<int, 1>{});
-            step(u + 2, std::integral_constant<int, 2>{});
+        if constexpr (STAGES == 3) {
+            for (; u + 2 < n_kt; u += 3) {
+                step(u, St0{});
+                step(u + 1, St1{});
+                step(u + 2, St2{});
+            }
+            if (u < n_kt) step(u, St0{});
+            if (u + 1 < n_kt) step(u + 1, St1{});
+        } else {
+            for (; u + 1 < n_kt; u += 2) {
+                step(u, St0{});
+                step(u + 1, St1{});
+            }
+            if (u < n_kt) step(u, St0{});
         }
-        if (u < n_kt) step(u, std::integral_constant<int, 0>{});
-        if (u + 1 < n_kt) step(u + 1, std::integral_constant<int, 1>{});
     }
 
     // epilogue: O = O~ / l, L = (m + log2 l) ln 2; a row with nothing kept
