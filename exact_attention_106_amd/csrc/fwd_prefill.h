@@ -103,6 +103,7 @@ constexpr int kScaleBlock = 128;
 // (loaded at the start of block j-1, converted to bf16 and stored before
 // block j).
 constexpr int kThreads3 = 256;
+constexpr int kPageWin = 128;   // paged: tiles per window of page ids held in LDS
 constexpr int kRing = 4;    // LDS stages of K and of V
 
 
@@ -258,6 +259,7 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
     constexpr int KC = L::KC, DT = L::DT, NFV = L::NFV, NFK = L::NFK;
     constexpr int NS_PV = L::NS_PV, NS_QK = L::NS_QK, NS = L::NS, PRE = L::PRE, MX = L::MX;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[L::LDS];
+    [[maybe_unused]] __shared__ int page_win[2][PAGED ? 4 * kPageWin : 1];   // paged: page ids, see fill_pages
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -382,12 +384,30 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
         vpage0 = V + (size_t)hd * (16 * L::VROW);
     }
     auto valid_rows = [&](int t) { return min(max(kmax - 16 * (4 * t + w), 0), 16); };
-    auto pid_of = [&](int t) -> int { return valid_rows(t) > 0 ? bt_s[4 * t + w] : 0; };
     auto page_rsrc = [&](const uint8_t *page0, int t, int pid) {
         return sgpr_rsrc(page0 + (size_t)pid * pg.page_stride, (uint32_t)valid_rows(t) * L::KROW);
     };
     [[maybe_unused]] u32x4 pk_cur{}, pv_cur{};   // copies of the current step: K(j+3), V(j+2)
     [[maybe_unused]] int p2 = 0, p3 = 0;         // pages of tiles j+2, j+3 for the next step
+    // Page ids come from LDS: a double-buffered window of the sequence's table
+    // row, kPageWin tiles (4 kPageWin entries, wave w's page of tile t at
+    // 4 (t mod kPageWin) + w), window c in buffer c mod 2. The prologue fills
+    // windows 0 and 1; the step of tile c kPageWin (c >= 1) fills window c + 1
+    // into the buffer of window c - 1, which every wave has left. Entries past
+    // the row read 0. (A global load of the entry inside the loop would be
+    // followed by a wait for every outstanding vector-memory operation, the
+    // ring's copies included.)
+    auto fill_pages = [&](int c) __attribute__((always_inline)) {
+        if constexpr (PAGED) {
+            for (int idx = tid; idx < 4 * kPageWin; idx += kThreads3) {
+                const long e = (long)c * 4 * kPageWin + idx;
+                page_win[c & 1][idx] = e < pg.max_blocks ? bt_s[e] : 0;
+            }
+        }
+    };
+    auto page_of = [&](int t) -> int {
+        return valid_rows(t) > 0 ? page_win[(t / kPageWin) & 1][4 * (t % kPageWin) + w] : 0;
+    };
     const uint32_t lds_k = (uint32_t)(size_t)smem;
     const uint32_t lds_v = lds_k + kRing * L::K_TILE;
     // this wave's share of a K / V tile in LDS (stage 0)
@@ -395,7 +415,7 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
     const uint32_t wv_base = __builtin_amdgcn_readfirstlane(lds_v + w * L::V_DMA * 1024);
     auto issue_k_part = [&](int j, int i) {
         if constexpr (PAGED)
-            dma16(page_rsrc(kpage0, j, pid_of(j)), wk_base + (uint32_t)(j & (kRing - 1)) * L::K_TILE + i * 1024,
+            dma16(page_rsrc(kpage0, j, page_of(j)), wk_base + (uint32_t)(j & (kRing - 1)) * L::K_TILE + i * 1024,
                   kpoff[i], 0u);
         else
             dma16(rk, wk_base + (uint32_t)(j & (kRing - 1)) * L::K_TILE + i * 1024, kdma_off[i],
@@ -419,7 +439,7 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
         if constexpr (FP8) {
             v8reg[i] = vload16(rv, v8_goff(i), soff);
         } else if constexpr (PAGED) {
-            dma16(page_rsrc(vpage0, j, pid_of(j)), wv_base + (uint32_t)(j & (kRing - 1)) * L::V_TILE + i * 1024,
+            dma16(page_rsrc(vpage0, j, page_of(j)), wv_base + (uint32_t)(j & (kRing - 1)) * L::V_TILE + i * 1024,
                   vpoff[i], 0u);
         } else {
             dma16(rv, wv_base + (uint32_t)(j & (kRing - 1)) * L::V_TILE + i * 1024, vdma_off[i], soff);
@@ -988,10 +1008,11 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
             vs_nx = vs_h[min(j + 1, n_tiles - 1) * kBC / kScaleBlock];
         }
         if constexpr (PAGED) {
+            p3 = page_of(j + 3);
             pv_cur = page_rsrc(vpage0, j + 2, p2);
             pk_cur = page_rsrc(kpage0, j + 3, p3);
             p2 = p3;
-            p3 = pid_of(j + 4);   // first used in the next step, after its barrier
+            if (j >= kPageWin && j % kPageWin == 0) fill_pages(j / kPageWin + 1);
         }
     };
 
@@ -1001,6 +1022,8 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
         vs_nx = vs_h[0];
     }
     for (int i = tid; i < L::LDS / 16; i += kThreads3) reinterpret_cast<u32x4 *>(smem)[i] = u32x4{};
+    fill_pages(0);
+    fill_pages(1);
     lds_barrier();
     if constexpr (FP8) {
 #pragma unroll
@@ -1011,6 +1034,7 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
         for (int i = 0; i < L::V8_LOADS; ++i) issue_v_part(0, i);
         wait_vm(2 * L::K_DMA + L::V8_LOADS);     // Q and K(0)
     } else {
+        if constexpr (PAGED) p2 = page_of(2);
 #pragma unroll
         for (int i = 0; i < L::K_DMA; ++i) issue_k_part(0, i);
 #pragma unroll
@@ -1021,10 +1045,6 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
         for (int i = 0; i < L::V_DMA; ++i) issue_v_part(1, i);
 #pragma unroll
         for (int i = 0; i < L::K_DMA; ++i) issue_k_part(2, i);
-        if constexpr (PAGED) {
-            p2 = pid_of(2);
-            p3 = pid_of(3);
-        }
         wait_vm(2 * L::K_DMA + 2 * L::V_DMA);     // Q and K(0)
     }
     // the loads are asm: pin their results after the wait (a copy placed
@@ -1087,6 +1107,7 @@ __global__ __launch_bounds__(kThreads3, 1) void fwd_kernel3(
     // their registers from being reused while in flight
 #pragma unroll
     for (int i = 0; i < L::V8_LOADS; ++i) asm volatile("" : "+v"(v8reg[i]));
+
     asm volatile("s_nop 15\n\ts_nop 15");
 
     // ---- epilogue: O = O~ / l ; L = (m + log2 l) ln 2 ----

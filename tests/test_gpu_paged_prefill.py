@@ -71,6 +71,22 @@ def test_paged_prefill_grids(gpu, S, H, n_new, ctx_lo, ctx_hi):
     assert np.array_equal(np.isneginf(l.cpu().numpy()), np.isneginf(rl)), "queries that see no key"
 
 
+def test_paged_prefill_long_contexts(gpu):
+    """Contexts of 33000-41000 tokens (up to ~640 key tiles): the kernel holds
+    the page ids in LDS windows of 128 tiles, refilled as it goes, so every
+    wave here reads windows 0-5, most of them refilled ones."""
+    p = inputs.paged_pool(num_seqs=2, H=1, d=128, ctx_lo=33000, ctx_hi=41000, seed=90)
+    q = inputs.dense(2, 1, 300, 128, seed=91).q
+    log("fa_paged_prefill S2 H1 n_new=300 ctx=%s" % p.ctx_lens.tolist())
+    assert int(p.ctx_lens.min()) > 5 * 128 * 64 // 2
+    o, l = fa.fa_paged_prefill(q.to(gpu), p.kcache.to(gpu), p.vcache.to(gpu), p.block_table.to(gpu),
+                               p.ctx_lens.to(gpu), scale=p.scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.paged_prefill(f64(q), bits(p.kcache), bits(p.vcache), p.block_table.numpy(),
+                                  p.ctx_lens.numpy(), p.scale)
+    check("paged prefill long contexts", o, l, ro, rl)
+
+
 def test_block_manager_fork_cow_prefill(gpu):
     """Prompt of 100 tokens, forked into three samples that each add 20 tokens:
     shared prompt pages, one copy-on-write per sample on the half-full last
