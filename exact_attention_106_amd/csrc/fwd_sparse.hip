@@ -15,10 +15,10 @@
 // (j / 4, i, b * H + h, 0); word j % 4 of the output is u, and P_ij is dropped
 // iff u < threshold = floor(p * 2^32).
 //
-// Structure as in the paged prefill kernel: workgroup = 4 waves x 32 queries
-// of one (b, h), XCD-aware order; the kept key blocks of the query block are
-// listed in LDS first, and their 64-key tiles stream through three LDS stages
-// by direct copies two tiles ahead; S^T = K Q^T with one query per lane,
+// Structure: workgroup = 4 waves x 32 queries of one (b, h), XCD-aware
+// order, two workgroups per CU; the kept key blocks of the query block are
+// listed in LDS first, and their 64-key tiles stream through two LDS stages
+// by direct copies one tile ahead; S^T = K Q^T with one query per lane,
 // online softmax with a lazy reference max, O^T += V^T P^T.
 #include "fa_device.h"
 #include "fa_dma.h"
@@ -61,22 +61,20 @@ __device__ __forceinline__ Philox philox4x32_10(uint32_t c0, uint32_t c1, uint32
     return Philox{{c0, c1, c2, c3}};
 }
 
-// Without dropout two workgroups share a CU (2 waves per SIMD, 256 registers,
-// a two-stage ring in 68 KiB of LDS): one workgroup's softmax runs while the
+// Two workgroups share a CU (2 waves per SIMD, at most 256 registers, a
+// two-stage ring in 68 KiB of LDS): one workgroup's softmax runs while the
 // other's MFMAs do, which a single wave's order (S, softmax, P V) does not
-// allow. Dropout's generator needs more registers than that: one workgroup per
-// CU, a three-stage ring, copies two tiles ahead.
+// allow.
 template <bool CAUSAL, bool DROPOUT>
-__global__ __launch_bounds__(kSpThreads) __attribute__((amdgpu_waves_per_eu(DROPOUT ? 1 : 2, DROPOUT ? 1 : 2))) void sparse_fwd_kernel(
+__global__ __launch_bounds__(kSpThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_fwd_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     const uint8_t *__restrict__ MASK, uint16_t *__restrict__ O, float *__restrict__ LSE, int N, int BH,
     int n_qb, float scale, uint32_t drop_threshold, float inv_keep, uint32_t seed_lo, uint32_t seed_hi)
 {
     constexpr int D = 128, ROW = 2 * D, CPR = D / 8, KC = D / 16, DT = D / 32;
     constexpr int TILE = kSpTile * ROW;
-    constexpr int STAGES = DROPOUT ? 3 : 2;
     constexpr int NDMA = TILE / 1024 / 4;          // 1 KiB copies per wave and tensor
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * 2 * TILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * 2 * TILE];
     __shared__ int16_t tiles[kSpMaxTiles];
     __shared__ int n_tiles_sh;
 
@@ -159,10 +157,12 @@ __global__ __launch_bounds__(kSpThreads) __attribute__((amdgpu_waves_per_eu(DROP
     float m = neg_inf(), lsum = 0.f;
     const float c = scale * kLog2e;
 
-    constexpr int NSD = 2 * KC, NST = NSD + 4 * DT, LA = DROPOUT ? 4 : 3;
-    auto tile = [&](int kt, auto sc, auto mc) __attribute__((always_inline)) {
+    constexpr int NSD = 2 * KC, NST = NSD + 4 * DT, LA = 4;
+    // One tile body for masked and unmasked tiles (the mask is a uniform
+    // branch around the masking): two inlined copies made the compiler give O
+    // different registers in each and copy all 64 accumulators at the join.
+    auto tile = [&](int kt, auto sc, bool masked) __attribute__((always_inline)) {
         constexpr int S = decltype(sc)::value;
-        constexpr bool MASKED = decltype(mc)::value;
         constexpr uint32_t KB = S * 2 * TILE, VB = KB + TILE;
         const uint8_t *lds = smem;
         const int k0 = kt * kSpTile;
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(kSpThreads) __attribute__((amdgpu_waves_per_eu(DROP
             }
         };
         auto softmax = [&]() __attribute__((always_inline)) {
-            if constexpr (MASKED) {
+            if (masked) {
                 // element 4a + b of half s2 is key k0 + 32 s2 + 8a + 4h + b;
                 // keys past N, and past the query when causal, are masked
                 const int lim = (CAUSAL ? min(my_q, N - 1) : N - 1) - (k0 + 4 * h);
@@ -248,57 +248,29 @@ __global__ __launch_bounds__(kSpThreads) __attribute__((amdgpu_waves_per_eu(DROP
     // List entry u uses LDS stage u mod 3; its step issues the copies of
     // entry u + 2 and ends once entry u + 1 is in LDS. A tile needs the mask
     // when it reaches past N or (causal) past the wave's first query.
-    // Two stages: entry u uses stage u mod 2; its step issues the copies of
-    // entry u + 1 into the other stage (free since the last barrier) and ends
-    // once they have landed. Three stages: entry u uses stage u mod 3; its
-    // step issues entry u + 2 and ends once entry u + 1 is in LDS. A tile
-    // needs the mask when it reaches past N or (causal) past the wave's first
-    // query.
-    constexpr int AHEAD = STAGES - 1;
+    // Entry u of the list uses LDS stage u mod 2; its step issues the copies
+    // of entry u + 1 into the other stage (free since the last barrier) and
+    // ends once they have landed. A tile needs the mask when it reaches past
+    // N or (causal) past the wave's first query.
     auto step = [&](int u, auto sc) __attribute__((always_inline)) {
         constexpr int S = decltype(sc)::value;
-        const bool ahead = u + AHEAD < n_kt;
-        if (ahead) issue(u + AHEAD, (S + AHEAD) % STAGES);
+        if (u + 1 < n_kt) issue(u + 1, S ^ 1);
         const int kt = __builtin_amdgcn_readfirstlane((int)tiles[u]);
         const int last_key = kt * kSpTile + kSpTile - 1;
-        if (last_key >= N || (CAUSAL && last_key > qw)) tile(kt, sc, std::true_type{});
-        else tile(kt, sc, std::false_type{});
-        if (AHEAD == 2 && ahead) wait_vm_n<2 * NDMA>();
-        else wait_vm_n<0>();
+        tile(kt, sc, last_key >= N || (CAUSAL && last_key > qw));
+        wait_vm_n<0>();
         __syncthreads();
     };
-    using St0 = std::integral_constant<int, 0>;
-    using St1 = std::integral_constant<int, 1>;
-    using St2 = std::integral_constant<int, 2>;
     if (n_kt > 0) {
         issue(0, 0);
-        if constexpr (STAGES == 3) {
-            if (1 < n_kt) {
-                issue(1, 1);
-                wait_vm_n<2 * NDMA>();
-            } else {
-                wait_vm_n<0>();
-            }
-        } else {
-            wait_vm_n<0>();
-        }
+        wait_vm_n<0>();
         __syncthreads();
         int u = 0;
-        if constexpr (STAGES == 3) {
-            for (; u + 2 < n_kt; u += 3) {
-                step(u, St0{});
-                step(u + 1, St1{});
-                step(u + 2, St2{});
-            }
-            if (u < n_kt) step(u, St0{});
-            if (u + 1 < n_kt) step(u + 1, St1{});
-        } else {
-            for (; u + 1 < n_kt; u += 2) {
-                step(u, St0{});
-                step(u + 1, St1{});
-            }
-            if (u < n_kt) step(u, St0{});
+        for (; u + 1 < n_kt; u += 2) {
+            step(u, std::integral_constant<int, 0>{});
+            step(u + 1, std::integral_constant<int, 1>{});
         }
+        if (u < n_kt) step(u, std::integral_constant<int, 0>{});
     }
 
     // epilogue: O = O~ / l, L = (m + log2 l) ln 2; a row with nothing kept
