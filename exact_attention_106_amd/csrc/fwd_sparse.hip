@@ -245,9 +245,6 @@ __global__ __launch_bounds__(kSpThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         });
     };
 
-    // List entry u uses LDS stage u mod 3; its step issues the copies of
-    // entry u + 2 and ends once entry u + 1 is in LDS. A tile needs the mask
-    // when it reaches past N or (causal) past the wave's first query.
     // Entry u of the list uses LDS stage u mod 2; its step issues the copies
     // of entry u + 1 into the other stage (free since the last barrier) and
     // ends once they have landed. A tile needs the mask when it reaches past
