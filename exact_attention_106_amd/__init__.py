@@ -22,7 +22,7 @@ from ._lib import FaError
 __all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_quantize_fp8", "fa_quantize_fp8_qkv", "fa_fwd_block_sparse", "fa_bwd", "fa_bwd_workspace_bytes",
            "fa_paged_decode", "fa_paged_decode_workspace_bytes", "fa_paged_decode_noalloc",
            "fa_noalloc_scratch_bytes", "fa_paged_prefill", "BlockManager",
-           "fa_copy_pages",
+           "fa_copy_pages", "fa_check_paged_tables",
            "fa_read_probe", "fa_status_str", "fa_version", "FaError"]
 
 
@@ -456,6 +456,26 @@ def fa_copy_pages(kcache: torch.Tensor, vcache: torch.Tensor, src: torch.Tensor,
     st = _lib.load().fa_copy_pages(_ptr(kcache), _ptr(vcache), _ptr(src), _ptr(dst), n, P, H, d, ps,
                                    _stream(kcache))
     _lib.check(st, "fa_copy_pages")
+
+
+@_on_device
+def fa_check_paged_tables(block_table: torch.Tensor, ctx_lens: torch.Tensor, page_size: int, num_pages: int,
+                          out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Check a block table and context lengths against the paged calls' contract
+    on the device. Returns a device int32 tensor [2]: the number of sequences that
+    break it, and the smallest such sequence index (-1 if none)."""
+    _check_dev("block_table", block_table, torch.int32)
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [S, max_blocks]")
+    S, max_blocks = block_table.shape
+    _check_dev("ctx_lens", ctx_lens, torch.int32, (S,))
+    if out is None:
+        out = torch.empty((2,), dtype=torch.int32, device=block_table.device)
+    _check_dev("out", out, torch.int32, (2,))
+    st = _lib.load().fa_check_paged_tables(_ptr(block_table), _ptr(ctx_lens), S, max_blocks, int(page_size),
+                                           int(num_pages), _ptr(out), _stream(block_table))
+    _lib.check(st, "fa_check_paged_tables")
+    return out
 
 
 @_on_device

@@ -22,7 +22,7 @@ EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_quantize_fp8", "fa_quantize
            "fa_bm_state_bytes", "fa_bm_init",
            "fa_bm_add_seq", "fa_bm_fork", "fa_bm_append_token", "fa_bm_free_seq",
            "fa_bm_num_free_pages", "fa_bm_seq_len", "fa_bm_page_refcount", "fa_bm_block_table",
-           "fa_copy_pages", "fa_read_probe", "fa_status_str", "fa_version")
+           "fa_copy_pages", "fa_check_paged_tables", "fa_read_probe", "fa_status_str", "fa_version")
 
 
 class FaError(RuntimeError):
@@ -94,6 +94,8 @@ def load() -> ctypes.CDLL:
         lib.fa_bm_block_table.restype = i
         lib.fa_copy_pages.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp]
         lib.fa_copy_pages.restype = i
+        lib.fa_check_paged_tables.argtypes = [vp, vp, i, i, i, i, vp, vp]
+        lib.fa_check_paged_tables.restype = i
         lib.fa_read_probe.argtypes = [vp, ctypes.c_size_t, vp, vp]
         lib.fa_read_probe.restype = i
         lib.fa_status_str.argtypes = [i]

@@ -1,4 +1,5 @@
-// Paged KV block manager (host) and the page copy of its copy-on-write.
+// Paged KV block manager (host), the page copy of its copy-on-write, and a
+// device check of block tables against the paged kernels' contract.
 //
 // PagedAttention ("FlashAttention系列优化", PagedAttention section): a
 // sequence's KV cache is cut into fixed-size blocks of tokens; a block table
@@ -70,6 +71,47 @@ __global__ __launch_bounds__(256) void copy_pages_kernel(uint8_t *__restrict__ k
     for (size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 16; i < page_bytes; i += (size_t)gridDim.x * 256 * 16) {
         *reinterpret_cast<fa::u32x4 *>(kc + t + i) = *reinterpret_cast<const fa::u32x4 *>(kc + s + i);
         *reinterpret_cast<fa::u32x4 *>(vc + t + i) = *reinterpret_cast<const fa::u32x4 *>(vc + s + i);
+    }
+}
+
+// result = {0, -1} before the check. A fill kernel rather than a memset, so
+// that the two launches of a check may be recorded into a HIP graph.
+__global__ void check_tables_init(int32_t *__restrict__ result)
+{
+    if (threadIdx.x == 0) {
+        result[0] = 0;
+        result[1] = -1;
+    }
+}
+
+// One wave per sequence: ctx_lens[s] must lie in [0, max_blocks * page_size]
+// and the first ceil(ctx_lens[s] / page_size) entries of its block-table row
+// in [0, num_pages). A sequence that breaks either adds 1 to result[0] and
+// lowers result[1] to its index (unsigned minimum, so -1 = 0xffffffff stands
+// for "none yet"). Entries past a sequence's used blocks are not read.
+__global__ __launch_bounds__(256) void check_tables_kernel(const int32_t *__restrict__ bt,
+                                                           const int32_t *__restrict__ ctx, int num_seqs,
+                                                           int max_blocks, int page_size, int num_pages,
+                                                           int32_t *__restrict__ result)
+{
+    const int lane = threadIdx.x & 63;
+    for (int s = blockIdx.x * 4 + (int)(threadIdx.x >> 6); s < num_seqs; s += gridDim.x * 4) {
+        const long long len = ctx[s];
+        bool bad = len < 0 || len > (long long)max_blocks * page_size;
+        if (!bad) {
+            const int used = (int)((len + page_size - 1) / page_size);
+            const int32_t *row = bt + (size_t)s * max_blocks;
+            bool lane_bad = false;
+            for (int e = lane; e < used; e += 64) {
+                const int32_t p = row[e];
+                lane_bad |= p < 0 || p >= num_pages;
+            }
+            bad = __any(lane_bad);
+        }
+        if (bad && lane == 0) {
+            atomicAdd(result, 1);
+            atomicMin(reinterpret_cast<unsigned *>(result + 1), (unsigned)s);
+        }
     }
 }
 
@@ -222,6 +264,22 @@ fa_status fa_copy_pages(void *kcache, void *vcache, const int32_t *src, const in
     const unsigned gx = (unsigned)((page_bytes / 16 + 255) / 256 < 64 ? (page_bytes / 16 + 255) / 256 : 64);
     hipLaunchKernelGGL(copy_pages_kernel, dim3(gx, (unsigned)n), dim3(256), 0, static_cast<hipStream_t>(stream),
                        static_cast<uint8_t *>(kcache), static_cast<uint8_t *>(vcache), src, dst, page_bytes);
+    return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_check_paged_tables(const int32_t *block_table, const int32_t *ctx_lens, int num_seqs,
+                                int max_blocks_per_seq, int page_size, int num_pages, int32_t *result,
+                                void *stream)
+{
+    if (!block_table || !ctx_lens || !result) return FA_ERR_NULL_PTR;
+    if (num_seqs <= 0 || max_blocks_per_seq <= 0 || page_size <= 0 || num_pages <= 0) return FA_ERR_BAD_SHAPE;
+    if (((uintptr_t)block_table | (uintptr_t)ctx_lens | (uintptr_t)result) & 3) return FA_ERR_UNSUPPORTED;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    hipLaunchKernelGGL(check_tables_init, dim3(1), dim3(64), 0, st, result);
+    if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
+    const long long wgs = ((long long)num_seqs + 3) / 4;
+    hipLaunchKernelGGL(check_tables_kernel, dim3((unsigned)(wgs < 1024 ? wgs : 1024)), dim3(256), 0, st,
+                       block_table, ctx_lens, num_seqs, max_blocks_per_seq, page_size, num_pages, result);
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

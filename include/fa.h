@@ -23,7 +23,8 @@
  *   - Arguments are checked on the host before anything is launched. A failed
  *     check returns its status and has no side effect. A launch failure
  *     returns FA_ERR_HIP. Device-side contracts (block_table entries, ctx_lens)
- *     are the caller's to keep and are not checked.
+ *     are the caller's to keep and are not checked by the attention calls;
+ *     fa_check_paged_tables checks them on the device when asked.
  *   - Stateless and re-entrant; calls on different streams may overlap.
  */
 #ifndef FA_H
@@ -305,6 +306,28 @@ fa_status fa_bm_block_table(const void *state, int32_t *block_table, int32_t *ct
  */
 fa_status fa_copy_pages(void *kcache, void *vcache, const int32_t *src, const int32_t *dst, int n,
                         int num_pages, int H, int d, int page_size, void *stream);
+
+/*
+ * Debug check of the paged calls' device-side contract (PagedAttention block
+ * table, "FlashAttention系列优化"): an entry outside the page pool makes
+ * fa_paged_decode / fa_paged_prefill read outside the caches, so a caller that
+ * builds tables itself can run this first, on the same stream.
+ *   block_table: device int32 [num_seqs, max_blocks_per_seq]
+ *   ctx_lens:    device int32 [num_seqs]
+ *   result:      device int32 [2], written by the call (contents on entry do
+ *                not matter): result[0] = number of sequences s whose
+ *                ctx_lens[s] is outside [0, max_blocks_per_seq * page_size]
+ *                or one of whose first ceil(ctx_lens[s] / page_size) entries
+ *                is outside [0, num_pages); result[1] = the smallest such s,
+ *                or -1 when there is none. Entries past a sequence's used
+ *                blocks are not read.
+ * Any page_size >= 1. Pointers 4-byte aligned (FA_ERR_UNSUPPORTED otherwise).
+ * Two kernel launches, no host synchronisation and no memset (so it may be
+ * recorded into a HIP graph); the caller reads result once the stream is done.
+ */
+fa_status fa_check_paged_tables(const int32_t *block_table, const int32_t *ctx_lens, int num_seqs,
+                                int max_blocks_per_seq, int page_size, int num_pages, int32_t *result,
+                                void *stream);
 
 /*
  * Measurement helper, not part of the attention path: reads bytes (a

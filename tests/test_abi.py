@@ -191,3 +191,19 @@ def test_paged_decode_noalloc_validation(lib):
     assert call(scale=0.0) == UNSUPPORTED
     assert call(mb=2497) == 8                       # FA_ERR_SCRATCH_LIMIT, before any launch
     assert call(S=65536) == BAD_SHAPE
+
+
+def test_check_paged_tables_validation(lib):
+    f = lib.fa_check_paged_tables
+
+    def call(bt=FAKE, ctx=FAKE, S=4, mb=8, ps=16, P=32, res=FAKE):
+        return f(bt, ctx, S, mb, ps, P, res, None)
+    assert call(bt=None) == NULL_PTR
+    assert call(ctx=None) == NULL_PTR
+    assert call(res=None) == NULL_PTR
+    assert call(S=0) == BAD_SHAPE
+    assert call(mb=-1) == BAD_SHAPE
+    assert call(ps=0) == BAD_SHAPE
+    assert call(P=0) == BAD_SHAPE
+    for n in ("bt", "ctx", "res"):
+        assert call(**{n: FAKE + 2}) == UNSUPPORTED, n   # 4-byte alignment

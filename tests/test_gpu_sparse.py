@@ -67,3 +67,21 @@ def test_block_sparse_full_mask_matches_fa_fwd(gpu):
     torch.cuda.synchronize()
     assert float((o1.float() - o2.float()).abs().max()) < 2e-2
     assert float((l1 - l2).abs().max()) < 1e-3
+
+
+def test_block_sparse_bitwise_repeatable(gpu):
+    """No floating-point atomics: two runs give the same bits, with and without
+    dropout; a different seed changes the dropped weights."""
+    x = inputs.dense(2, 2, 1030, 128, seed=951)
+    q, k, v = x.q.to(gpu), x.k.to(gpu), x.v.to(gpu)
+    rng = np.random.default_rng(3)
+    mask = torch.from_numpy((rng.random((9, 9)) < 0.6).astype(np.uint8)).to(gpu)
+    log("fa_fwd_block_sparse repeat B2 H2 N1030")
+    for p_drop in (0.0, 0.2):
+        a = fa.fa_fwd_block_sparse(q, k, v, mask, scale=x.scale, causal=True, dropout_p=p_drop, seed=77)
+        b = fa.fa_fwd_block_sparse(q, k, v, mask, scale=x.scale, causal=True, dropout_p=p_drop, seed=77)
+        torch.cuda.synchronize()
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]), p_drop
+    c = fa.fa_fwd_block_sparse(q, k, v, mask, scale=x.scale, causal=True, dropout_p=0.2, seed=78)
+    torch.cuda.synchronize()
+    assert not torch.equal(a[0], c[0])
