@@ -116,6 +116,38 @@ def dense(B: int, H: int, N: int, d: int, seed: int, dtype: str = "bf16",
     return Dense(*tensors, scale=scale, causal=causal, name=name or f"dense_{dtype}_B{B}H{H}N{N}d{d}")
 
 
+def dense_on_device(B: int, H: int, N: int, d: int, seed: int, device, scale: Optional[float] = None,
+                    causal: bool = False, name: str = "") -> Dense:
+    """Standard-normal bf16 Q, K, V drawn directly on the device by torch's
+    seeded generator, for sizes whose host generation would take minutes (up
+    to the 2^31 - 1 elements per tensor that the dense entry points accept).
+    Not the same values as dense() for the same seed; the same seed on the
+    same device gives the same tensors."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    tensors = [torch.randn((B, H, N, d), generator=g, device=device, dtype=torch.bfloat16) for _ in range(3)]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    return Dense(*tensors, scale=scale, causal=causal, name=name or f"dense_dev_bf16_B{B}H{H}N{N}d{d}")
+
+
+def fp8_on_device(B: int, H: int, N: int, d: int, seed: int, device, causal: bool = False,
+                  name: str = "") -> Fp8:
+    """E4M3 codes and per-block scales drawn on the device, for the largest
+    sizes: codes are torch's float8_e4m3fn cast of 8 * N(0, 1) draws (|x| far
+    below 448, so no NaN code), every block scale uniform in [1/16, 1/8), so
+    the values are about N(0, 1). Not the block quantisation of bf16 inputs
+    that fp8_inputs() performs."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    nsb = (N + FP8_BLOCK - 1) // FP8_BLOCK
+    codes = [(8 * torch.randn((B, H, N, d), generator=g, device=device)).to(torch.float8_e4m3fn)
+             .view(torch.uint8) for _ in range(3)]
+    scales = [(1 + torch.rand((B, H, nsb), generator=g, device=device)) / 16 for _ in range(3)]
+    return Fp8(*codes, *scales, scale=1.0 / math.sqrt(d), causal=causal,
+               name=name or f"fp8_dev_B{B}H{H}N{N}d{d}")
+
+
 def grad_out(B: int, H: int, N: int, d: int, seed: int, device="cpu") -> torch.Tensor:
     """Seeded upstream gradient dO for the backward pass: standard normal, bf16."""
     rng = np.random.Generator(np.random.PCG64(seed))

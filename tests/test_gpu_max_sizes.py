@@ -1,0 +1,120 @@
+"""The largest sizes the C ABI accepts (B*H*N*d <= 2^31 - 1 elements per
+tensor), through fa_fwd, fa_fwd_fp8 and fa_bwd, against the fp64 oracle on
+sampled rows (and, for the backward, sampled keys).
+
+Two shapes push the addressing to its limits: 8192 heads of 2047 tokens (the
+last head starts 4.29e9 bytes into each bf16 tensor; ragged last row block),
+and a single causal head of 8,388,808 tokens (2.15e9 bytes, past 2^31, with
+the last K/V tiles beyond byte offset 2^31 of the head and a ragged tail).
+Tolerances as for the other tests of each path: bf16 O max-abs 2e-2, FP8
+8e-2 + half a bf16 ulp, L 1e-3; backward as in test_gpu_bwd."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import exact_attention_106_amd as fa
+from exact_attention_106_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+MAX_ELEMS = (1 << 31) - 1
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def f64(t):
+    return oracle.bf16_bits_to_f64(t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16))
+
+
+def check(name, o, l, ro, rl):
+    got_o, got_l = f64(o), l.cpu().double().numpy()
+    assert np.all(np.isfinite(got_o)), name + ": non-finite O"
+    eo = float(np.max(np.abs(got_o - ro)))
+    el = float(np.max(np.abs(got_l - rl)))
+    log("%s: max|dO|=%.3e max|dL|=%.3e" % (name, eo, el))
+    assert eo <= 2e-2 and el <= 1e-3, name
+
+
+def test_fwd_most_heads(gpu):
+    B, H, N, d = 2, 4096, 2047, 128
+    assert B * H * N * d <= MAX_ELEMS < B * H * (N + 1) * d
+    log("fa_fwd bf16 B%d H%d N%d d%d non-causal (ABI maximum elements)" % (B, H, N, d))
+    x = inputs.dense_on_device(B, H, N, d, seed=4242, device=gpu)
+    o, l = fa.fa_fwd(x.q, x.k, x.v, scale=x.scale, causal=False)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 255, 256, 1791, 1792, 2046])
+    for b, h in ((0, 0), (0, 4095), (1, 1234), (1, 4095)):
+        ro, rl = oracle.attention_rows(f64(x.q[b, h, rows]), rows, f64(x.k[b, h]), f64(x.v[b, h]), x.scale, False)
+        check("b%d h%d" % (b, h), o[b, h, rows], l[b, h, rows], ro, rl)
+
+
+def test_fwd_longest_head(gpu):
+    N, d = 8_388_808, 128
+    assert N * d <= MAX_ELEMS and N * d * 2 > 1 << 31 and N % 256 == 200
+    log("fa_fwd bf16 B1 H1 N%d d%d causal (one head past 2^31 bytes)" % (N, d))
+    x = inputs.dense_on_device(1, 1, N, d, seed=4243, device=gpu, causal=True)
+    o, l = fa.fa_fwd(x.q, x.k, x.v, scale=x.scale, causal=True)
+    torch.cuda.synchronize()
+    log("  kernel done; oracle on sampled rows")
+    rows = np.array([0, 1, 1 << 22, (1 << 23) - 1, 1 << 23, N - 100, N - 1])
+    ro, rl = oracle.attention_rows(f64(x.q[0, 0, rows]), rows, f64(x.k[0, 0]), f64(x.v[0, 0]), x.scale, True)
+    check("N%d causal" % N, o[0, 0, rows], l[0, 0, rows], ro, rl)
+    # A row that sees millions of keys averages them down to |O| ~ 1e-3, where
+    # the absolute bound says nothing (O = 0 would meet it); such rows are held
+    # to the same 2e-2 relative to the row's largest |O|.
+    got = f64(o[0, 0, rows])
+    for r, i in enumerate(rows):
+        if i >= 1 << 22:
+            peak = float(np.abs(ro[r]).max())
+            rel = float(np.abs(got[r] - ro[r]).max()) / peak
+            log("  row %d: max|O_ref| %.3e, max|dO| / max|O_ref| = %.3e" % (i, peak, rel))
+            assert rel <= 2e-2, i
+
+
+def test_fp8_most_heads(gpu):
+    B, H, N, d = 2, 4096, 2047, 128
+    log("fa_fwd_fp8 B%d H%d N%d d%d causal (ABI maximum elements)" % (B, H, N, d))
+    x = inputs.fp8_on_device(B, H, N, d, seed=4244, device=gpu, causal=True)
+    o, l = fa.fa_fwd_fp8(x.q8, x.k8, x.v8, x.q_scale, x.k_scale, x.v_scale, scale=x.scale, causal=True)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 255, 256, 1791, 1792, 2046])
+    for b, h in ((0, 0), (1, 4095)):
+        q, k, v = (oracle.dequant_e4m3(c[b, h].cpu().numpy(), s[b, h].cpu().numpy())
+                   for c, s in ((x.q8, x.q_scale), (x.k8, x.k_scale), (x.v8, x.v_scale)))
+        ro, rl = oracle.attention_rows(q[rows], rows, k, v, x.scale, True)
+        got_o, got_l = f64(o[b, h, rows]), l[b, h, rows].cpu().double().numpy()
+        e = np.abs(got_o - ro)
+        tol = 8e-2 + 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ro), 2.0 ** -126))) - 8)
+        log("fp8 b%d h%d: max|dO|=%.3e max|dL|=%.3e" % (b, h, float(e.max()), float(np.abs(got_l - rl).max())))
+        assert np.all(np.isfinite(got_o)) and np.all(e <= tol)
+        assert float(np.abs(got_l - rl).max()) <= 1e-3
+
+
+def test_bwd_most_heads(gpu):
+    """fa_bwd with 8192 heads of 2047 tokens: dq on sampled rows, dk and dv on
+    sampled keys of the first and last heads, against the oracle's chain rule
+    (tolerance per tensor as in the other backward tests: 1e-2 * max|ref| +
+    half a bf16 ulp + 1e-5, with max|ref| taken over the sampled entries)."""
+    B, H, N, d = 2, 4096, 2047, 128
+    log("fa_bwd bf16 B%d H%d N%d d%d causal (ABI maximum elements)" % (B, H, N, d))
+    x = inputs.dense_on_device(B, H, N, d, seed=4245, device=gpu, causal=True)
+    do = inputs.dense_on_device(B, H, N, d, seed=4246, device=gpu).q
+    o, lse = fa.fa_fwd(x.q, x.k, x.v, scale=x.scale, causal=True)
+    dq, dk, dv = fa.fa_bwd(x.q, x.k, x.v, o, lse, do, scale=x.scale, causal=True)
+    torch.cuda.synchronize()
+    idx = np.array([0, 1, 127, 128, 1000, 1920, 2046])
+    for b, h in ((0, 0), (1, 4095)):
+        q, k, v, g = (f64(t[b, h]) for t in (x.q, x.k, x.v, do))
+        rq = oracle.attention_bwd_rows(q, k, v, g, idx, x.scale, True)
+        rk, rv = oracle.attention_bwd_cols(q, k, v, g, idx, x.scale, True)
+        for nm, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+            got = f64(got[b, h, idx])
+            err = np.abs(got - ref)
+            tol = 1e-2 * float(np.abs(ref).max()) + 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -126))) - 8) + 1e-5
+            log("bwd b%d h%d %s: max err %.3e (max|ref| %.3e)" % (b, h, nm, float(err.max()), float(np.abs(ref).max())))
+            assert np.all(np.isfinite(got)) and np.all(err <= tol), nm
