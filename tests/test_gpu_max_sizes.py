@@ -1,6 +1,7 @@
-"""The largest sizes the C ABI accepts (B*H*N*d <= 2^31 - 1 elements per
-tensor), through fa_fwd, fa_fwd_fp8 and fa_bwd, against the fp64 oracle on
-sampled rows (and, for the backward, sampled keys).
+"""The largest sizes the C ABI accepts, against the fp64 oracle: B*H*N*d <=
+2^31 - 1 elements per tensor through fa_fwd, fa_fwd_fp8 and fa_bwd (sampled
+rows, and for the backward sampled keys), 65535 sequences through
+fa_paged_decode and 65535 sequence-heads through fa_paged_prefill.
 
 Two shapes push the addressing to its limits: 8192 heads of 2047 tokens (the
 last head starts 4.29e9 bytes into each bf16 tensor; ragged last row block),
@@ -118,3 +119,47 @@ def test_bwd_most_heads(gpu):
             tol = 1e-2 * float(np.abs(ref).max()) + 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -126))) - 8) + 1e-5
             log("bwd b%d h%d %s: max err %.3e (max|ref| %.3e)" % (b, h, nm, float(err.max()), float(np.abs(ref).max())))
             assert np.all(np.isfinite(got)) and np.all(err <= tol), nm
+
+
+def bits16(t):
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def test_decode_most_sequences(gpu):
+    """fa_paged_decode with 65535 sequences (the most it accepts) of 1..100
+    tokens, pairs sharing prompt pages, NaN page tails: every sequence against
+    the oracle; the table also passes fa_check_paged_tables."""
+    p = inputs.paged_pool(num_seqs=65535, H=2, d=128, ctx_lo=1, ctx_hi=100, seed=4247, share=0.5, device=gpu)
+    log("fa_paged_decode S65535 H2 d128 ctx 1..100 (most sequences), %d pages" % p.n_unique_pages)
+    chk = fa.fa_check_paged_tables(p.block_table, p.ctx_lens, 16, p.kcache.shape[0])
+    o, l = fa.fa_paged_decode(p.q, p.kcache, p.vcache, p.block_table, p.ctx_lens, scale=p.scale)
+    torch.cuda.synchronize()
+    assert chk.cpu().tolist() == [0, -1]
+    ro, rl = oracle.paged_decode(f64(p.q), bits16(p.kcache), bits16(p.vcache), p.block_table.cpu().numpy(),
+                                 p.ctx_lens.cpu().numpy(), p.scale)
+    check("decode S65535", o, l, ro, rl)
+
+
+def test_paged_prefill_most_sequence_heads(gpu):
+    """fa_paged_prefill with num_seqs * H = 65535 (the most it accepts): 65535
+    sequences of 1..100 tokens, the 3 newest of each as queries (those at
+    negative positions see nothing: O = 0, L = -inf); 400 sequences, the last
+    ones among them, against the oracle."""
+    S, n_new = 65535, 3
+    p = inputs.paged_pool(num_seqs=S, H=1, d=128, ctx_lo=1, ctx_hi=100, seed=4248, share=0.5, device=gpu)
+    q = inputs.dense_on_device(S, 1, n_new, 128, seed=4249, device=gpu).q
+    log("fa_paged_prefill S65535 H1 n_new3 d128 (most sequence-heads)")
+    o, l = fa.fa_paged_prefill(q, p.kcache, p.vcache, p.block_table, p.ctx_lens, scale=p.scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    sel = np.unique(np.concatenate([rng.choice(S - 8, 392, replace=False), np.arange(S - 8, S)]))
+    ro, rl = oracle.paged_prefill(f64(q[sel]), bits16(p.kcache), bits16(p.vcache),
+                                  p.block_table.cpu().numpy()[sel], p.ctx_lens.cpu().numpy()[sel], p.scale)
+    got_o, got_l = f64(o[sel]), l[sel].cpu().double().numpy()
+    fin = np.isfinite(rl)
+    assert np.array_equal(np.isfinite(got_l), fin) and (~fin).any()
+    assert np.all(got_o[~fin] == 0)
+    eo = float(np.max(np.abs(got_o - ro)))
+    el = float(np.max(np.abs(got_l[fin] - rl[fin])))
+    log("paged prefill S65535: max|dO|=%.3e max|dL|=%.3e" % (eo, el))
+    assert eo <= 2e-2 and el <= 1e-3
