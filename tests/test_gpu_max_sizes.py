@@ -1,7 +1,7 @@
 """The largest sizes the C ABI accepts, against the fp64 oracle: B*H*N*d <=
-2^31 - 1 elements per tensor through fa_fwd, fa_fwd_fp8 and fa_bwd (sampled
-rows, and for the backward sampled keys), 65535 sequences through
-fa_paged_decode and 65535 sequence-heads through fa_paged_prefill.
+2^31 - 1 elements per tensor through fa_fwd, fa_fwd_fp8, fa_fwd_block_sparse
+and fa_bwd (sampled rows, and for the backward sampled keys), 65535 sequences
+through fa_paged_decode and 65535 sequence-heads through fa_paged_prefill.
 
 Two shapes push the addressing to its limits: 8192 heads of 2047 tokens (the
 last head starts 4.29e9 bytes into each bf16 tensor; ragged last row block),
@@ -163,3 +163,26 @@ def test_paged_prefill_most_sequence_heads(gpu):
     el = float(np.max(np.abs(got_l[fin] - rl[fin])))
     log("paged prefill S65535: max|dO|=%.3e max|dL|=%.3e" % (eo, el))
     assert eo <= 2e-2 and el <= 1e-3
+
+
+def test_block_sparse_most_heads(gpu):
+    """fa_fwd_block_sparse with 8192 heads of 2047 tokens, half the causal
+    blocks kept, dropout 0.1 (the last head's counter carries b*H + h = 8191):
+    sampled rows of the first and last heads. O bound 2e-2 / (1 - p)."""
+    from oracle import sparse
+    B, H, N, d, p_drop, seed = 2, 4096, 2047, 128, 0.1, 0x0123_4567_89AB_CDEF
+    log("fa_fwd_block_sparse B%d H%d N%d d%d causal p=%.1f (ABI maximum elements)" % (B, H, N, d, p_drop))
+    x = inputs.dense_on_device(B, H, N, d, seed=4250, device=gpu, causal=True)
+    mask = inputs.block_mask(N, density=0.5, seed=4251, causal=True)
+    o, l = fa.fa_fwd_block_sparse(x.q, x.k, x.v, mask.to(gpu), scale=x.scale, causal=True, dropout_p=p_drop,
+                                  seed=seed)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 255, 256, 1791, 1792, 2046])
+    for b, h in ((0, 0), (1, 4095)):
+        ro, rl = sparse.block_sparse_attention_rows(f64(x.q[b, h, rows]), rows, f64(x.k[b, h]), f64(x.v[b, h]),
+                                                    mask.numpy(), x.scale, True, bh=b * H + h, p_drop=p_drop,
+                                                    seed=seed)
+        got_o, got_l = f64(o[b, h, rows]), l[b, h, rows].cpu().double().numpy()
+        eo, el = float(np.abs(got_o - ro).max()), float(np.abs(got_l - rl).max())
+        log("sparse b%d h%d: max|dO|=%.3e max|dL|=%.3e" % (b, h, eo, el))
+        assert np.all(np.isfinite(got_o)) and eo <= 2e-2 / (1 - p_drop) and el <= 1e-3
