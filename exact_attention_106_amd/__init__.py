@@ -19,7 +19,7 @@ import torch
 from . import _lib
 from ._lib import FaError
 
-__all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_quantize_fp8", "fa_quantize_fp8_qkv", "fa_fwd_block_sparse", "fa_bwd", "fa_bwd_workspace_bytes",
+__all__ = ["attention", "fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_quantize_fp8", "fa_quantize_fp8_qkv", "fa_fwd_block_sparse", "fa_bwd", "fa_bwd_workspace_bytes",
            "fa_paged_decode", "fa_paged_decode_workspace_bytes", "fa_paged_decode_noalloc",
            "fa_noalloc_scratch_bytes", "fa_paged_prefill", "BlockManager",
            "fa_copy_pages", "fa_check_paged_tables",
@@ -273,6 +273,32 @@ def fa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, l
                             int(bool(causal)), _ptr(workspace), nbytes, _stream(q))
     _lib.check(st, "fa_bwd")
     return grads[0], grads[1], grads[2]
+
+
+class _Attention(torch.autograd.Function):
+    """fa_fwd forward, fa_bwd backward (O and L kept from the forward)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, scale, causal):
+        o, lse = fa_fwd(q, k, v, scale=scale, causal=causal)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.scale, ctx.causal = scale, causal
+        return o
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = fa_bwd(q, k, v, o, lse, dout.to(torch.bfloat16).contiguous(), scale=ctx.scale,
+                            causal=ctx.causal)
+        return dq, dk, dv, None, None
+
+
+def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float] = None,
+              causal: bool = False) -> torch.Tensor:
+    """Exact attention O = softmax(scale * Q K^T) V (bf16 [B, H, N, d], d in {64,
+    128}) as a differentiable torch op: the forward is fa_fwd, the gradient
+    fa_bwd with the forward's O and L, so a model can train through it."""
+    return _Attention.apply(q, k, v, scale, bool(causal))
 
 
 def fa_paged_decode_workspace_bytes(num_seqs: int, H: int, d: int, page_size: int,

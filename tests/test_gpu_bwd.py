@@ -111,3 +111,27 @@ def test_bwd_rejects_bad_arguments(fa, gpu):
     lse = torch.empty((1, 1, 64), dtype=torch.float32, device=gpu)
     with pytest.raises(fa.FaError):
         fa.fa_bwd(t, t, t, o, lse, t)
+
+
+def test_attention_autograd_matches_direct_calls(fa, gpu):
+    """fa.attention as a torch op: its O and the gradients autograd returns are
+    bit for bit those of fa_fwd and fa_bwd called directly with dO = G (the
+    gradient of sum(O * G) with respect to O), also when the gradient reaching
+    O is a non-contiguous view (second case, through a transpose)."""
+    for B, H, N, d, causal, via_t in ((1, 2, 333, 128, True, False), (2, 1, 200, 64, False, True)):
+        log("attention autograd B%d H%d N%d d%d causal=%d" % (B, H, N, d, causal))
+        x = inputs.dense(B, H, N, d, seed=710 + N)
+        g = inputs.grad_out(B, H, N, d, seed=711 + N).to(gpu)
+        q, k, v = (t.to(gpu).requires_grad_() for t in (x.q, x.k, x.v))
+        o = fa.attention(q, k, v, scale=x.scale, causal=causal)
+        if via_t:
+            (o.transpose(1, 2).float() * g.transpose(1, 2).float()).sum().backward()
+        else:
+            (o.float() * g.float()).sum().backward()
+        qd, kd, vd = q.detach(), k.detach(), v.detach()
+        o2, l2 = fa.fa_fwd(qd, kd, vd, scale=x.scale, causal=causal)
+        dq, dk, dv = fa.fa_bwd(qd, kd, vd, o2, l2, g, scale=x.scale, causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(o.detach(), o2)
+        for nm, got, want in (("dq", q.grad, dq), ("dk", k.grad, dk), ("dv", v.grad, dv)):
+            assert torch.equal(got, want), nm
