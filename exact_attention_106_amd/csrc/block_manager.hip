@@ -95,7 +95,7 @@ __global__ __launch_bounds__(256) void check_tables_kernel(const int32_t *__rest
                                                            int32_t *__restrict__ result)
 {
     const int lane = threadIdx.x & 63;
-    for (int s = blockIdx.x * 4 + (int)(threadIdx.x >> 6); s < num_seqs; s += gridDim.x * 4) {
+    for (long long s = blockIdx.x * 4ll + (threadIdx.x >> 6); s < num_seqs; s += gridDim.x * 4ll) {
         const long long len = ctx[s];
         bool bad = len < 0 || len > (long long)max_blocks * page_size;
         if (!bad) {
