@@ -128,11 +128,24 @@ fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o, con
                                         static_cast<hipStream_t>(stream)));
 }
 
+}  // extern "C"
+
+// The decode's chunk count num_seqs * ceil(max_blocks / 32) and its hash table
+// (a power of two of at least twice that) index in 32-bit ints: at most 2^29
+// chunks (65535 sequences of up to 262144 blocks = 4.2M tokens each).
+static bool decode_chunks_ok(int num_seqs, int max_blocks_per_seq)
+{
+    return (long long)num_seqs * fa::decode_max_splits(max_blocks_per_seq) <= (1LL << 29);
+}
+
+extern "C" {
+
 size_t fa_paged_decode_workspace_bytes(int num_seqs, int H, int d, int page_size,
                                        int max_blocks_per_seq)
 {
     if (num_seqs <= 0 || H <= 0 || max_blocks_per_seq <= 0) return 0;
     if (d != 128 || page_size != 16) return 0;
+    if (!decode_chunks_ok(num_seqs, max_blocks_per_seq)) return 0;
     return fa::decode_workspace_bytes(num_seqs, H, max_blocks_per_seq);
 }
 
@@ -148,6 +161,7 @@ static fa_status check_paged_decode(const void *q, const void *kcache, const voi
     if (d != 128 || page_size != 16) return FA_ERR_UNSUPPORTED;
     if (num_seqs > 65535 || H > 65535) return FA_ERR_BAD_SHAPE;
     if ((long long)max_blocks_per_seq * page_size > kMaxElems) return FA_ERR_BAD_SHAPE;
+    if (!decode_chunks_ok(num_seqs, max_blocks_per_seq)) return FA_ERR_BAD_SHAPE;
     if (bad_scale(scale)) return FA_ERR_UNSUPPORTED;
     return FA_OK;
 }

@@ -208,8 +208,11 @@ size_t fa_paged_decode_workspace_bytes(int num_seqs, int H, int d, int page_size
  *   o:        bf16 [num_seqs, H, d];  lse: fp32 [num_seqs, H] or NULL.
  *   workspace: device memory of at least fa_paged_decode_workspace_bytes(...)
  *             bytes; contents on entry do not matter.
- * d == 128, page_size == 16. ctx_lens and block_table are read only on the
- * device (no host synchronisation).
+ * d == 128, page_size == 16, num_seqs and H <= 65535, and at most 2^29
+ * chunks of 32 blocks: num_seqs * ceil(max_blocks_per_seq / 32) <= 2^29 (e.g.
+ * 65535 sequences of up to 262144 blocks); FA_ERR_BAD_SHAPE otherwise, and
+ * fa_paged_decode_workspace_bytes returns 0. ctx_lens and block_table are read
+ * only on the device (no host synchronisation).
  */
 fa_status fa_paged_decode(const void *q, const void *kcache, const void *vcache,
                           const int32_t *block_table, const int32_t *ctx_lens,

@@ -207,3 +207,19 @@ def test_check_paged_tables_validation(lib):
     assert call(P=0) == BAD_SHAPE
     for n in ("bt", "ctx", "res"):
         assert call(**{n: FAKE + 2}) == UNSUPPORTED, n   # 4-byte alignment
+
+
+def test_paged_decode_chunk_bound(lib):
+    # at most 2^29 chunks of 32 blocks (the decode's 32-bit chunk indexing)
+    ws = lib.fa_paged_decode_workspace_bytes
+    assert ws(65535, 1, 128, 16, 262144) > 0
+    assert ws(65535, 1, 128, 16, 262145) == 0
+    assert ws(64, 1, 128, 16, 100_000_000) > 0
+
+    def call(S, mb):
+        return lib.fa_paged_decode(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, S, 1, 128, 16, mb, 10, 0.1,
+                                   FAKE, 0, None)
+    assert call(65535, 262145) == BAD_SHAPE
+    assert call(65535, 262144) == WORKSPACE      # passes the shape checks, fails on the 0-byte workspace
+    assert lib.fa_paged_decode_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 65535, 1, 128, 16, 262145, 10,
+                                       0.1, None) == BAD_SHAPE
