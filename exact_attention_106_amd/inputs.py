@@ -135,7 +135,7 @@ def fp8_on_device(B: int, H: int, N: int, d: int, seed: int, device, causal: boo
                   name: str = "") -> Fp8:
     """E4M3 codes and per-block scales drawn on the device, for the largest
     sizes: codes are torch's float8_e4m3fn cast of 8 * N(0, 1) draws (|x| far
-    below 448, so no NaN code), every block scale uniform in [1/16, 1/8), so
+    below 448, so no NaN code), every block scale uniform in [1/16, 1/8], so
     the values are about N(0, 1). Not the block quantisation of bf16 inputs
     that fp8_inputs() performs."""
     g = torch.Generator(device=device)

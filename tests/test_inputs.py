@@ -90,3 +90,24 @@ def test_paged_pool_invariants():
             assert torch.isfinite(p.kcache[last, :, :rem]).all()
     q = inputs.paged_pool(num_seqs=10, H=2, d=8, ctx_lo=1, ctx_hi=200, seed=9, share=0.3)
     assert inputs.sha256_of(p.kcache, p.vcache, p.block_table) == inputs.sha256_of(q.kcache, q.vcache, q.block_table)
+
+
+def test_device_generators_seeded_and_in_range():
+    """dense_on_device / fp8_on_device (run here on the CPU device): the same
+    seed gives the same tensors, another seed others; E4M3 codes never NaN
+    (0x7f / 0xff); block scales in [1/16, 1/8]."""
+    a = inputs.dense_on_device(2, 3, 50, 64, seed=1, device="cpu")
+    b = inputs.dense_on_device(2, 3, 50, 64, seed=1, device="cpu")
+    c = inputs.dense_on_device(2, 3, 50, 64, seed=2, device="cpu")
+    assert a.q.dtype == torch.bfloat16 and tuple(a.q.shape) == (2, 3, 50, 64)
+    assert torch.equal(a.q, b.q) and torch.equal(a.v, b.v) and not torch.equal(a.q, c.q)
+    assert abs(float(a.q.float().std()) - 1.0) < 0.1
+    f = inputs.fp8_on_device(2, 3, 300, 128, seed=3, device="cpu")
+    g = inputs.fp8_on_device(2, 3, 300, 128, seed=3, device="cpu")
+    assert torch.equal(f.q8, g.q8) and torch.equal(f.v_scale, g.v_scale)
+    for codes in (f.q8, f.k8, f.v8):
+        assert codes.dtype == torch.uint8 and tuple(codes.shape) == (2, 3, 300, 128)
+        assert not ((codes & 0x7F) == 0x7F).any()
+    for s in (f.q_scale, f.k_scale, f.v_scale):
+        assert tuple(s.shape) == (2, 3, 3)
+        assert float(s.min()) >= 1 / 16 and float(s.max()) <= 1 / 8
