@@ -18,8 +18,9 @@
  *     stream must belong to it.
  *   - Tensors are dense row-major: q/k/v/o [B, H, N, d], lse [B, H, N] fp32.
  *   - Natural logarithms; L is in the units of the scaled scores.
- *   - causal != 0: key j is visible to query i iff j <= i (top-left aligned,
- *     diagonal visible; queries and keys have the same length N).
+ *   - causal is 0 or 1 (FA_ERR_UNSUPPORTED otherwise); causal = 1: key j is
+ *     visible to query i iff j <= i (top-left aligned, diagonal visible;
+ *     queries and keys have the same length N).
  *   - Arguments are checked on the host before anything is launched. A failed
  *     check returns its status and has no side effect. A launch failure
  *     returns FA_ERR_HIP. Device-side contracts (block_table entries, ctx_lens)
@@ -136,7 +137,7 @@ fa_status fa_quantize_fp8_qkv(const void *q, const void *k, const void *v, const
  * pairs that block_mask keeps; blocks are 128 x 128 tokens.
  *   block_mask: device uint8 [nb, nb], nb = ceil(N / 128), shared by every
  *     batch and head; entry [i][j] != 0 keeps key block j for query block i.
- *     With causal != 0, keys after the query are masked as well. A query with
+ *     With causal = 1, keys after the query are masked as well. A query with
  *     no kept key gets O = 0 and L = -inf.
  *   dropout_p in [0, 1): each softmax weight P_ij is kept with probability
  *     1 - dropout_p and scaled by 1 / (1 - dropout_p) (the "masking and
